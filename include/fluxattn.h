@@ -1,0 +1,158 @@
+/*
+ * fluxattn — joint-attention block of FLUX-style MM-DiT image generators on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The block, as NVIDIA's blog post "Speed up image generation with FLUX 3
+ * Image Klein on NVIDIA Blackwell GPUs" describes it:
+ *   - section "Running FLUX 3 inference with TensorRT LLM VisualGen": the text,
+ *     noisy-target-image and optional reference-image token streams are
+ *     processed separately and merged by one joint attention over all tokens;
+ *   - section "GEMM kernel optimization": query/key normalisation and rotary
+ *     position embedding (RoPE) follow the QKV projection;
+ *   - section "Quantized and sparse attention": dense BF16 attention is the
+ *     dominant kernel at 2048x2048, and FP8 queries/keys and values are a
+ *     supported attention precision.
+ * The pages give no formulas.  This library uses the plain readings:
+ *   RMSNorm   y_d = x_d * w_d / sqrt(mean_d(x^2) + eps), one fp32 weight
+ *             vector for Q and one for K, shared over batch, heads, streams;
+ *   RoPE      head dims split into contiguous (t, h, w) blocks of
+ *             (axes_t, axes_h, axes_w); inside axis a's block the adjacent
+ *             pair (y[2j], y[2j+1]) = (u, v) is rotated to
+ *             (u cos phi - v sin phi, u sin phi + v cos phi),
+ *             phi = pos_a * theta^(-2j/axes_a); V is not rotated;
+ *   attention O = softmax(Q' K'^T * softmax_scale) V, non-causal, no mask.
+ *
+ * Conventions shared by every entry point
+ *   Layout     row-major contiguous [B, H, N, D]; element (b,h,n,d) sits at
+ *              ((b*H + h)*N + n)*D + d.  pos_ids is int32 [N, 3] = (t, h, w)
+ *              per token, shared by all B and H.  Scales are fp32 [B, H].
+ *   Pointers   all data pointers are DEVICE pointers on the current HIP device.
+ *              The caller owns every buffer.  The library keeps no per-call
+ *              state, allocates nothing and never synchronises; work is
+ *              enqueued on `stream` (a hipStream_t; NULL = null stream) and
+ *              the call returns at once.
+ *   Shapes     D == 128; B, H, N >= 1; N <= FLUXATTN_MAX_N; axes even and
+ *              summing to D; theta > 0; eps >= 0.
+ *   Alignment  q/k/v/o and prologue outputs 16 bytes; pos_ids, weights and
+ *              scales 4 bytes.
+ *   Errors     validation order: null pointers, shape, alignment, aliasing,
+ *              device (must be gfx950).  Any failure returns before anything
+ *              is enqueued and leaves every output untouched.  A failed
+ *              launch returns FLUXATTN_ERR_HIP (fluxattn_last_hip_error()
+ *              gives the hipError_t).  Faults inside a kernel surface at the
+ *              caller's next synchronisation, as with any HIP work.
+ *   Numerics   inputs are not checked for NaN/Inf; a NaN spreads to the rows
+ *              it touches.  No atomics are used: results are bitwise
+ *              reproducible run to run.
+ *   Threads    every entry point is re-entrant and thread-safe.
+ */
+#ifndef FLUXATTN_H
+#define FLUXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLUXATTN_HEAD_DIM 128
+#define FLUXATTN_MAX_N (1 << 22)
+
+typedef enum {
+    FLUXATTN_OK = 0,
+    FLUXATTN_ERR_NULL_POINTER = 1,  /* a required pointer is NULL            */
+    FLUXATTN_ERR_INVALID_SHAPE = 2, /* B/H/N/D/axes/theta/eps out of range   */
+    FLUXATTN_ERR_MISALIGNED = 3,    /* a pointer breaks the alignment rule   */
+    FLUXATTN_ERR_ALIASING = 4,      /* an output overlaps a buffer it may not */
+    FLUXATTN_ERR_NO_DEVICE = 5,     /* no HIP device, or it is not gfx950    */
+    FLUXATTN_ERR_HIP = 6            /* a HIP call (launch) failed            */
+} fluxattn_status;
+
+/*
+ * Fused per-head RMSNorm + 3-axis RoPE on queries and keys, bf16.
+ * (blog post above, section "GEMM kernel optimization".)
+ *   q, k          bf16 [B,H,N,D] inputs.
+ *   q_out, k_out  bf16 [B,H,N,D] outputs, round-to-nearest-even.  q_out may
+ *                 equal q and k_out may equal k (in place); any other
+ *                 overlap between an output and another buffer is
+ *                 FLUXATTN_ERR_ALIASING.
+ *   q_norm_w, k_norm_w  fp32 [D] RMSNorm weights.
+ *   pos_ids       int32 [N,3] (t,h,w) token positions.
+ *   axes_*, theta RoPE axis split and base (FLUX: 16, 56, 56 and 1e4).
+ *   eps           RMSNorm epsilon (FLUX: 1e-6), inside the square root.
+ * Rotation angles are evaluated in fp32 from the integer ids and fp32
+ * frequencies (rounded from fp64 on the host); sums of squares are fp32.
+ */
+fluxattn_status fluxattn_qk_norm_rope_bf16(
+    const void *q, const void *k, void *q_out, void *k_out,
+    const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    void *stream);
+
+/*
+ * The same prologue on OCP FP8 E4M3 (e4m3fn: bias 7, max 448, no Inf)
+ * inputs with per-(b,h) dequantisation scales: x = e4m3(code) * scale[b,h].
+ * (blog post above, sections "GEMM kernel optimization" and "Quantized and
+ * sparse attention".)
+ *   q, k                    uint8 E4M3 codes [B,H,N,D].
+ *   q_scale, k_scale        fp32 [B,H] input scales.
+ *   q_out, k_out            uint8 E4M3 codes [B,H,N,D]; may equal q / k.
+ *   q_scale_out, k_scale_out fp32 [B,H], written by the kernel with
+ *                 sqrt(D) * max|w| / 448 for the matching weight vector.
+ *                 Every prologue output is bounded by sqrt(D) * max|w| in
+ *                 magnitude, so the encode never saturates.
+ * Other arguments as in fluxattn_qk_norm_rope_bf16.
+ */
+fluxattn_status fluxattn_qk_norm_rope_fp8(
+    const uint8_t *q, const uint8_t *k, const float *q_scale,
+    const float *k_scale, uint8_t *q_out, uint8_t *k_out, float *q_scale_out,
+    float *k_scale_out, const float *q_norm_w, const float *k_norm_w,
+    const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    void *stream);
+
+/*
+ * Non-causal joint attention O = softmax(Q K^T * softmax_scale) V over all N
+ * tokens of each (b,h), bf16 in and out.  (blog post above, sections
+ * "Running FLUX 3 inference with TensorRT LLM VisualGen" and "Quantized and
+ * sparse attention".)
+ *   q, k, v   bf16 [B,H,N,D] (q and k normally come out of the prologue).
+ *   o         bf16 [B,H,N,D] output; must not overlap q, k or v.
+ *   softmax_scale  <= 0 selects 1/sqrt(D).
+ * Scores and the softmax run in fp32; softmax probabilities are rounded to
+ * bf16 for the P.V product and the normaliser sums those rounded values;
+ * O is accumulated in fp32 and rounded once to bf16.  The N x N score matrix
+ * is never stored.
+ */
+fluxattn_status fluxattn_forward_bf16(
+    const void *q, const void *k, const void *v, void *o,
+    int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
+    void *stream);
+
+/*
+ * Joint attention on E4M3 queries, keys and values with per-(b,h) scales:
+ * Q = e4m3(q)*q_scale[b,h], and likewise K and V.  Output o is bf16
+ * [B,H,N,D] and must not overlap q, k or v.  (blog post above, section
+ * "Quantized and sparse attention": FP8 for both the QK and the V operands.)
+ */
+fluxattn_status fluxattn_forward_fp8(
+    const uint8_t *q, const uint8_t *k, const uint8_t *v,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    void *o, int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
+    void *stream);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char *fluxattn_status_string(fluxattn_status s);
+
+/* hipError_t of this thread's most recent FLUXATTN_ERR_HIP (0 if none). */
+int fluxattn_last_hip_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fluxattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUXATTN_H */

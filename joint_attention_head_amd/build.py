@@ -1,0 +1,77 @@
+"""Build libfluxattn.so in-tree with hipcc for gfx950.
+
+    python -m joint_attention_head_amd.build        # compiles every time
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfluxattn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+SOURCES = ["api.hip", "prologue.hip", "attention.hip"]
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    # packed fp32 VALU ops stay disabled in all device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libfluxattn)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile all HIP sources and link libfluxattn.so next to this file."""
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="fluxattn_build_")
+    try:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        for cmd, p in procs:
+            out, _ = p.communicate()
+            out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+            if p.returncode != 0:
+                raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+            if verbose and out.strip():
+                print(out)
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, LIB_PATH) if os.stat(tmp).st_dev == os.stat(PKG).st_dev else shutil.move(tmp_lib, LIB_PATH)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

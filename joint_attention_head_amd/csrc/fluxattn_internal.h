@@ -1,0 +1,50 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fluxattn {
+
+constexpr int kHeadDim = 128;
+constexpr int kPairs = kHeadDim / 2;
+
+// Per head-dimension pair p (dims 2p, 2p+1): which position axis rotates it
+// and its fp32 frequency theta^(-2j/axes_a) (computed in fp64 on the host).
+struct RopeTable {
+  float freq[kPairs];
+  int8_t axis[kPairs];
+};
+
+struct PrologueArgs {
+  const void *q, *k;
+  void *q_out, *k_out;
+  const float *w_q, *w_k;
+  const int32_t *pos;
+  const float *q_scale, *k_scale;     // fp8 only
+  float *q_scale_out, *k_scale_out;   // fp8 only
+  int64_t BH;                         // B * H
+  int32_t N;
+  float eps;
+};
+
+struct ForwardArgs {
+  const void *q, *k, *v;
+  void *o;
+  const float *q_scale, *k_scale, *v_scale;  // fp8 only
+  int32_t BH;
+  int32_t N;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
+                                hipStream_t s);
+hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
+                               hipStream_t s);
+hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s);
+
+// Workgroups the forward kernel launches for B*H heads of N tokens.
+int64_t forward_grid_blocks(int64_t BH, int64_t N);
+
+}  // namespace fluxattn

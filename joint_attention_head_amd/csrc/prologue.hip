@@ -1,0 +1,230 @@
+// Fused per-head RMSNorm + 3-axis RoPE on queries and keys (gfx950).
+//
+// The QKV projection of a FLUX-style MM-DiT block is followed by query/key
+// normalisation and a rotary position embedding (NVIDIA blog post "Speed up
+// image generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
+// "GEMM kernel optimization").  This kernel is the standalone form of that
+// step; it is bound by HBM bandwidth (about 1.5 flop per byte).
+//
+// Work decomposition: a 256-thread block owns 16 consecutive tokens.  Lane
+// group g (16 lanes) holds token g, and lane c of the group owns head dims
+// [8c, 8c+8) = rotation pairs 4c..4c+3.  The four rotation angles of a lane
+// depend only on its token, so their sin/cos are evaluated once and reused
+// for all B*H rows of Q and of K.  For a fixed (b,h) the block reads and
+// writes one contiguous 4 KiB (bf16) or 2 KiB (fp8) span.
+#include "fluxattn_internal.h"
+
+namespace fluxattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokensPerBlock = kThreads / 16;
+constexpr int kUnroll = 4;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;  // v_cvt_pk_bf16_f32: round to nearest even
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// DPP moves inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a DPP row: xor 1, xor 2 (quad permutes), then the
+// half-row mirror (lane i <-> 7-i) and the row mirror (lane i <-> 15-i).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+// Normalise and rotate the 8 values of one lane: f holds x (dequantised),
+// w the lane's 8 weights, cs/sn the 4 pair angles.  rstd comes from the sum
+// of squares over the whole 128-dim row.
+__device__ __forceinline__ void norm_rope8(float (&f)[8], const float (&w)[8],
+                                           const float (&cs)[4], const float (&sn)[4],
+                                           float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(f[i], f[i], ss);
+  ss = row16_sum(ss);
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u = f[2 * i] * w[2 * i] * rstd;
+    const float v = f[2 * i + 1] * w[2 * i + 1] * rstd;
+    f[2 * i] = u * cs[i] - v * sn[i];
+    f[2 * i + 1] = u * sn[i] + v * cs[i];
+  }
+}
+
+__device__ __forceinline__ void lane_angles(const PrologueArgs &a, const RopeTable &t,
+                                            int tok, int c, float (&cs)[4], float (&sn)[4]) {
+  const int32_t p0 = a.pos[3 * (int64_t)tok + 0];
+  const int32_t p1 = a.pos[3 * (int64_t)tok + 1];
+  const int32_t p2 = a.pos[3 * (int64_t)tok + 2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pr = 4 * c + i;
+    const int ax = t.axis[pr];
+    const int32_t p = ax == 0 ? p0 : (ax == 1 ? p1 : p2);
+    const float ang = (float)p * t.freq[pr];
+    sincosf(ang, &sn[i], &cs[i]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a, RopeTable t) {
+  const int c = threadIdx.x & 15;
+  const int tok = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 4);
+  if (tok >= a.N) return;  // the 16 lanes of a token leave together
+
+  float cs[4], sn[4];
+  lane_angles(a, t, tok, c, cs, sn);
+
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t *src = static_cast<const uint16_t *>(which ? a.k : a.q);
+    uint16_t *dst = static_cast<uint16_t *>(which ? a.k_out : a.q_out);
+    const float *wp = which ? a.w_k : a.w_q;
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
+
+    const int64_t row_stride = (int64_t)a.N * kHeadDim;
+    const int64_t base = (int64_t)tok * kHeadDim + 8 * c;
+    for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+      uint4 x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (bh0 + u < a.BH)
+          x[u] = *reinterpret_cast<const uint4 *>(src + (bh0 + u) * row_stride + base);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (bh0 + u >= a.BH) break;
+        float f[8] = {bf16_lo(x[u].x), bf16_hi(x[u].x), bf16_lo(x[u].y), bf16_hi(x[u].y),
+                      bf16_lo(x[u].z), bf16_hi(x[u].z), bf16_lo(x[u].w), bf16_hi(x[u].w)};
+        norm_rope8(f, w, cs, sn, a.eps);
+        uint4 y;
+        y.x = pack_bf16(f[0], f[1]);
+        y.y = pack_bf16(f[2], f[3]);
+        y.z = pack_bf16(f[4], f[5]);
+        y.w = pack_bf16(f[6], f[7]);
+        *reinterpret_cast<uint4 *>(dst + (bh0 + u) * row_stride + base) = y;
+      }
+    }
+  }
+}
+
+// OCP E4M3 pair decode / encode with the gfx950 conversion instructions.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *f) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(const float *f) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
+  return (uint32_t)w;
+}
+
+__global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, RopeTable t) {
+  const int lane = threadIdx.x & 63;
+  // Output scale sqrt(D) * max|w| / 448: every output lies within +-448 of it.
+  float sq, sk;
+  {
+    const float mq = wave_max(fmaxf(fabsf(a.w_q[lane]), fabsf(a.w_q[lane + 64])));
+    const float mk = wave_max(fmaxf(fabsf(a.w_k[lane]), fabsf(a.w_k[lane + 64])));
+    const float root_d = 11.313708498984760f;  // sqrt(128)
+    sq = mq > 0.f ? root_d * mq / 448.f : 1.f;
+    sk = mk > 0.f ? root_d * mk / 448.f : 1.f;
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t i = threadIdx.x; i < a.BH; i += kThreads) {
+      a.q_scale_out[i] = sq;
+      a.k_scale_out[i] = sk;
+    }
+  }
+  const int c = threadIdx.x & 15;
+  const int tok = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 4);
+  if (tok >= a.N) return;
+
+  float cs[4], sn[4];
+  lane_angles(a, t, tok, c, cs, sn);
+
+  for (int which = 0; which < 2; ++which) {
+    const uint8_t *src = static_cast<const uint8_t *>(which ? a.k : a.q);
+    uint8_t *dst = static_cast<uint8_t *>(which ? a.k_out : a.q_out);
+    const float *wp = which ? a.w_k : a.w_q;
+    const float *s_in = which ? a.k_scale : a.q_scale;
+    const float inv_out = 1.0f / (which ? sk : sq);
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
+
+    const int64_t row_stride = (int64_t)a.N * kHeadDim;
+    const int64_t base = (int64_t)tok * kHeadDim + 8 * c;
+    for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+      uint2 x[kUnroll];
+      float s[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (bh0 + u < a.BH) {
+          x[u] = *reinterpret_cast<const uint2 *>(src + (bh0 + u) * row_stride + base);
+          s[u] = s_in[bh0 + u];
+        }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (bh0 + u >= a.BH) break;
+        float f[8];
+        e4m3x4_to_f32(x[u].x, f);
+        e4m3x4_to_f32(x[u].y, f + 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] *= s[u];
+        norm_rope8(f, w, cs, sn, a.eps);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(f[i] * inv_out, -448.f), 448.f);
+        uint2 y;
+        y.x = f32x4_to_e4m3(f);
+        y.y = f32x4_to_e4m3(f + 4);
+        *reinterpret_cast<uint2 *>(dst + (bh0 + u) * row_stride + base) = y;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
+  const dim3 grid((a.N + kTokensPerBlock - 1) / kTokensPerBlock);
+  hipLaunchKernelGGL(prologue_bf16_kernel, grid, dim3(kThreads), 0, s, a, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
+  const dim3 grid((a.N + kTokensPerBlock - 1) / kTokensPerBlock);
+  hipLaunchKernelGGL(prologue_fp8_kernel, grid, dim3(kThreads), 0, s, a, t);
+  return hipGetLastError();
+}
+
+}  // namespace fluxattn

@@ -47,7 +47,8 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) -> float64.  A bf16 value is the upper
     16 bits of the IEEE binary32 value, so the decode is a shift."""
     b32 = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16)
-    return b32.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # NaN patterns stay NaN
+        return b32.view(np.float32).astype(np.float64)
 
 
 def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:

@@ -1,0 +1,317 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Small workloads are compared element by element; the 2048x2048 workloads
+(N = 16896 bf16 and N = 33280 fp8) run in full on the GPU in the same launch
+configuration the benchmark times and are compared on sampled (b, h, row)
+outputs that the oracle computes one head at a time.  Tolerances for the
+attention output are max-abs 2e-2 / mean-abs 2e-3 (bf16) and 4e-2 / 4e-3
+(fp8); the prologue is held to its rounding bound (see each test).
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_head_amd as fa
+import oracle
+from workloads import (ROPE_AXES, custom_workload, make_inputs, make_peaked_inputs)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BF16_TOL = (2e-2, 2e-3)
+FP8_TOL = (4e-2, 4e-3)
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+@functools.lru_cache(maxsize=4)
+def inputs(name):
+    return make_inputs(name)
+
+
+def small(B, H, n_txt, grid, ref_grid=None, dtype="bf16", seed=0):
+    return make_inputs(custom_workload(B, H, n_txt, grid, ref_grid, dtype, seed))
+
+
+def dev(t):
+    return t.to(DEV).contiguous()
+
+
+def f64(t, scale=None):
+    return oracle.torch_to_f64(t.cpu() if t.is_cuda else t,
+                               None if scale is None else scale.cpu())
+
+
+def check_close(got, ref, tol, what):
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    _flush(f"{what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} rel_l2={rel:.3e}")
+    assert np.isfinite(got).all(), what
+    assert err.max() <= tol[0], (what, err.max())
+    assert err.mean() <= tol[1], (what, err.mean())
+    return rel
+
+
+def sample_rows(N, k=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(min(32, N)), np.arange(max(0, N - 48), N),
+                           rng.choice(N, size=min(k, N), replace=False)])
+    return np.unique(rows)
+
+
+# ------------------------------------------------------------------ prologue
+
+def prologue_ref(inp):
+    if inp.q.dtype == torch.float8_e4m3fn:
+        q, k = f64(inp.q, inp.q_scale), f64(inp.k, inp.k_scale)
+    else:
+        q, k = f64(inp.q), f64(inp.k)
+    return oracle.qk_prologue(q, k, inp.w_q.double().numpy(), inp.w_k.double().numpy(),
+                              inp.pos.numpy())
+
+
+def pair_norm(y):
+    n = np.sqrt(y[..., 0::2] ** 2 + y[..., 1::2] ** 2)
+    return np.repeat(n, 2, axis=-1)
+
+
+PROLOGUE_CASES = {
+    "tiny": lambda: inputs("tiny"),
+    "flux_dev_512": lambda: inputs("flux_dev_512"),
+    "odd_77+256": lambda: small(1, 3, 77, (16, 16)),
+    "ref_t1_tiny": lambda: small(2, 2, 7, (4, 5), (3, 4)),
+}
+
+
+@pytest.mark.parametrize("case", list(PROLOGUE_CASES))
+def test_prologue_bf16_parity(case):
+    _flush(f"prologue bf16 {case}")
+    inp = PROLOGUE_CASES[case]()
+    qo, ko = fa.fluxattn_qk_norm_rope_bf16(dev(inp.q), dev(inp.k), dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    rq, rk = prologue_ref(inp)
+    for got, ref, name in ((f64(qo), rq, "q"), (f64(ko), rk, "k")):
+        # bf16 RNE (<= 2^-8 relative) plus fp32 angle / sum-of-squares error
+        bound = 2.0 ** -8 * np.abs(ref) + 4e-5 * np.maximum(pair_norm(ref), 1.0)
+        bad = np.abs(got - ref) > bound
+        _flush(f"  {name}: max_err={np.abs(got - ref).max():.3e} violations={bad.sum()}")
+        assert not bad.any()
+
+
+def test_prologue_bf16_in_place_matches_out_of_place():
+    inp = inputs("tiny")
+    q, k = dev(inp.q), dev(inp.k)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    qo, ko = fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos)
+    q2, k2 = q.clone(), k.clone()
+    fa.fluxattn_qk_norm_rope_bf16(q2, k2, w_q, w_k, pos, q_out=q2, k_out=k2)
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(ko.view(torch.int16), k2.view(torch.int16))
+
+
+def test_prologue_position_zero_is_norm_only_and_rms_invariant():
+    inp = small(1, 2, 8, (8, 8))
+    pos = torch.zeros_like(inp.pos)
+    c = 0.75
+    w = torch.full((128,), c)
+    qo, ko = fa.fluxattn_qk_norm_rope_bf16(dev(inp.q), dev(inp.k), dev(w), dev(w), dev(pos))
+    torch.cuda.synchronize()
+    ref = oracle.rms_norm(f64(inp.q), np.full(128, c), 1e-6)
+    got = f64(qo)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+    rms = np.sqrt(np.mean(f64(ko) ** 2, axis=-1))
+    np.testing.assert_allclose(rms, c, rtol=4e-3)
+
+
+@pytest.mark.parametrize("case", ["tiny_fp8", "ref_t1_fp8"])
+def test_prologue_fp8_parity(case):
+    _flush(f"prologue fp8 {case}")
+    inp = small(1, 2, 64, (16, 16), None, "fp8") if case == "tiny_fp8" else \
+        small(1, 3, 9, (5, 6), (4, 4), "fp8", seed=3)
+    qo, ko, sqo, sko = fa.fluxattn_qk_norm_rope_fp8(dev(inp.q), dev(inp.k), dev(inp.q_scale),
+                                                    dev(inp.k_scale), dev(inp.w_q), dev(inp.w_k),
+                                                    dev(inp.pos))
+    torch.cuda.synchronize()
+    rq, rk = prologue_ref(inp)
+    for got8, s_out, ref, w, name in ((qo, sqo, rq, inp.w_q, "q"), (ko, sko, rk, inp.w_k, "k")):
+        s_ref = oracle.fp8_prologue_out_scale(w.double().numpy())
+        np.testing.assert_allclose(s_out.cpu().double().numpy(), s_ref, rtol=1e-6)
+        got = f64(got8, s_out)
+        # E4M3 RNE: <= 2^-4 relative for normals, 2^-10 * scale for subnormals
+        bound = 2.0 ** -4 * np.abs(ref) + 2.0 ** -10 * s_ref + 4e-5 * np.maximum(pair_norm(ref), 1.0)
+        bad = np.abs(got - ref) > bound
+        _flush(f"  {name}: max_err={np.abs(got - ref).max():.3e} violations={bad.sum()}")
+        assert not bad.any()
+        assert np.abs(got).max() <= 448 * float(s_out.max()) + 1e-6
+
+
+# ------------------------------------------------------------------ forward
+
+def run_forward_bf16(inp, **kw):
+    return fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), dev(inp.v), **kw)
+
+
+FORWARD_CASES = {
+    "tiny": lambda: inputs("tiny"),
+    "flux_dev_512": lambda: inputs("flux_dev_512"),
+    "odd_77+256": lambda: small(1, 3, 77, (16, 16)),
+    "n1": lambda: small(1, 2, 1, (0, 0)),
+    "n65": lambda: small(2, 1, 1, (8, 8)),
+    "n129": lambda: small(1, 1, 1, (8, 16)),
+    "peaked_1024": lambda: make_peaked_inputs("flux_dev_1024"),
+}
+
+
+@pytest.mark.parametrize("case", list(FORWARD_CASES))
+def test_forward_bf16_parity(case):
+    _flush(f"forward bf16 {case}")
+    inp = FORWARD_CASES[case]()
+    o = run_forward_bf16(inp)
+    torch.cuda.synchronize()
+    if inp.q.shape[2] > 2000:
+        rows = sample_rows(inp.q.shape[2])
+        ref = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v), rows=rows)
+        got = f64(o)[:, :, rows]
+    else:
+        ref = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v))
+        got = f64(o)
+    rel = check_close(got, ref, BF16_TOL, f"forward bf16 {case}")
+    assert rel < 1e-2
+
+
+def test_forward_bf16_custom_scale():
+    inp = small(1, 2, 5, (10, 10))
+    o = run_forward_bf16(inp, softmax_scale=0.05)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v), scale=0.05)
+    check_close(f64(o), ref, BF16_TOL, "forward bf16 scale=0.05")
+
+
+def test_forward_bf16_invariants():
+    inp = small(1, 2, 13, (10, 10))
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    # V == 1 gives exactly 1
+    o = fa.fluxattn_forward_bf16(q, k, torch.ones_like(v))
+    # identical keys give the mean of V
+    k_same = k[:, :, :1].expand_as(k).contiguous()
+    o2 = fa.fluxattn_forward_bf16(q, k_same, v)
+    # bitwise reproducible
+    a = fa.fluxattn_forward_bf16(q, k, v)
+    b = fa.fluxattn_forward_bf16(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.all(o == 1.0)
+    mean_v = f64(inp.v).mean(axis=2, keepdims=True)
+    check_close(f64(o2), np.broadcast_to(mean_v, o2.shape), BF16_TOL, "identical keys")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_forward_bf16_writes_every_output_and_nothing_else():
+    inp = small(1, 3, 50, (9, 7))
+    B, H, N, D = inp.q.shape
+    n = B * H * N * D
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    o = buf[guard:guard + n].view(B, H, N, D)
+    fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), dev(inp.v), o=o)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+
+
+def test_forward_bf16_key_permutation_invariance():
+    inp = small(1, 2, 11, (12, 12))
+    perm = torch.randperm(inp.q.shape[2], generator=torch.Generator().manual_seed(1))
+    a = run_forward_bf16(inp)
+    b = fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k[:, :, perm]), dev(inp.v[:, :, perm]))
+    torch.cuda.synchronize()
+    check_close(f64(b), f64(a), BF16_TOL, "key permutation")
+
+
+# ------------------------------------------------------------------ joint
+
+def joint_ref(inp, heads=None, rows=None):
+    sc = lambda t, s: f64(t, s) if t.dtype == torch.float8_e4m3fn else f64(t)
+    w_q, w_k, pos = inp.w_q.double().numpy(), inp.w_k.double().numpy(), inp.pos.numpy()
+    if heads is None:
+        return oracle.joint_attention(sc(inp.q, inp.q_scale), sc(inp.k, inp.k_scale),
+                                      sc(inp.v, inp.v_scale), w_q, w_k, pos, rows=rows)
+    out = []
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        s = lambda x: None if x is None else x[sl]
+        out.append(oracle.joint_attention(sc(inp.q[sl], s(inp.q_scale)), sc(inp.k[sl], s(inp.k_scale)),
+                                          sc(inp.v[sl], s(inp.v_scale)), w_q, w_k, pos, rows=rows)[0, 0])
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux_dev_512", "flux_dev_1024"])
+def test_joint_bf16_parity_full(name):
+    _flush(f"joint bf16 {name}")
+    inp = inputs(name)
+    o = fa.joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    check_close(f64(o), joint_ref(inp), BF16_TOL, f"joint bf16 {name}")
+
+
+def test_joint_bf16_parity_t2i_2048_sampled():
+    _flush("joint bf16 t2i_2048_cfg (N=16896, B=2, H=24)")
+    inp = inputs("t2i_2048_cfg")
+    o = fa.joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    heads = [(0, 0), (1, 23), (0, 13)]
+    rows = sample_rows(inp.q.shape[2])
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    rel = check_close(got, joint_ref(inp, heads, rows), BF16_TOL, "joint bf16 t2i sampled")
+    assert rel < 1e-2
+    # V == 1 on the full-size launch
+    ones = fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), torch.ones_like(o))
+    torch.cuda.synchronize()
+    assert torch.all(ones == 1.0)
+
+
+def test_forward_fp8_parity_tiny_and_ragged():
+    for inp in (small(1, 2, 64, (16, 16), None, "fp8"), small(1, 3, 77, (16, 16), None, "fp8", seed=2)):
+        o = fa.fluxattn_forward_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale),
+                                    dev(inp.k_scale), dev(inp.v_scale))
+        torch.cuda.synchronize()
+        ref = oracle.attention(f64(inp.q, inp.q_scale), f64(inp.k, inp.k_scale), f64(inp.v, inp.v_scale))
+        check_close(f64(o), ref, FP8_TOL, f"forward fp8 N={inp.q.shape[2]}")
+
+
+def test_joint_fp8_parity_tiny():
+    inp = small(1, 2, 64, (16, 16), (8, 8), "fp8")
+    o = fa.joint_attention_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale),
+                               dev(inp.v_scale), dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    rel = check_close(f64(o), joint_ref(inp), FP8_TOL, "joint fp8 tiny")
+    assert rel < 1e-1
+
+
+def test_fp8_i2i_2048_sampled():
+    _flush("fp8 i2i_2048 (N=33280, H=24)")
+    inp = inputs("i2i_2048")
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    sq, sk, sv = dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale)
+    heads = [(0, 0), (0, 17)]
+    rows = sample_rows(inp.q.shape[2], k=64)
+    # attention alone on the generated fp8 tensors
+    o = fa.fluxattn_forward_fp8(q, k, v, sq, sk, sv)
+    torch.cuda.synchronize()
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    ref = np.stack([oracle.attention(f64(inp.q[b:b + 1, h:h + 1], inp.q_scale[b:b + 1, h:h + 1]),
+                                     f64(inp.k[b:b + 1, h:h + 1], inp.k_scale[b:b + 1, h:h + 1]),
+                                     f64(inp.v[b:b + 1, h:h + 1], inp.v_scale[b:b + 1, h:h + 1]),
+                                     rows=rows)[0, 0] for (b, h) in heads])
+    check_close(got, ref, FP8_TOL, "forward fp8 i2i sampled")
+    # the whole block
+    o = fa.joint_attention_fp8(q, k, v, sq, sk, sv, dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fp8 i2i sampled")
+    assert rel < 1e-1
