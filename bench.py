@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Joint-attention throughput on one MI355X.
+
+One step = the whole hot path over one batch: the fused QK-RMSNorm + 3-axis
+RoPE prologue, then non-causal softmax attention, on the 2048x2048
+text-to-image workload with CFG (B=2, H=24, N = 512 text + 128x128 image
+tokens = 16896, d=128, bf16), inputs already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Prints one JSON line: TFLOP/s of the step (4*B*H*N^2*d per step), the
+attention kernel's roofline fraction (its own average launch time from HIP
+events on the launch stream), the same figures at N=4608 (FLUX-dev 1024x1024)
+under "also", and the fp64 CPU oracle timed on a bounded sample of the same
+workload under "cpu_baseline".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_t2i_2048_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "joint_attention_head_amd", "csrc", f)
+                  for f in ("attention.hip", "fluxattn_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, or None if the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="t2i_2048_cfg")
+    p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=3, help="(b,h) heads in the CPU oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def run_gpu(name: str, steps: int, warmup: int):
+    import torch
+
+    import joint_attention_head_amd as fa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    w_q, w_k, pos = inp.w_q.to(dev), inp.w_k.to(dev), inp.pos.to(dev)
+    qn, kn, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos, q_out=qn, k_out=kn, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pro = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
+    fwd = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
+    span = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3
+    assert torch.isfinite(o).all().item()
+    flops = w.flops
+    prologue_bytes = 4.0 * w.B * w.H * w.N * 128 * 2      # read + write Q and K
+    attn_min_bytes = 4.0 * w.B * w.H * w.N * 128 * 2      # read Q, K, V, write O once
+    t_fwd = sum(fwd) / len(fwd)
+    t_pro = sum(pro) / len(pro)
+    res = {
+        "workload": w,
+        "ms_per_step": wall / steps * 1e3,
+        "gpu_span_ms_per_step": span / steps * 1e3,
+        "value": flops / (wall / steps) / 1e12,
+        "forward_ms": t_fwd * 1e3,
+        "forward_tflops": flops / t_fwd / 1e12,
+        "prologue_us": t_pro * 1e6,
+        "prologue_gbs": prologue_bytes / t_pro / 1e9,
+        "attn_min_bytes": attn_min_bytes,
+        "flops": flops,
+    }
+    del q, k, v, qn, kn, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 29                        # 2^29 bf16 = 1 GiB read + 1 GiB written
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"copy calibration: torch.neg over {n * 2} bytes read and {n * 2} written", file=sys.stderr)
+
+
+def cpu_baseline(name: str, n_heads: int):
+    import numpy as np
+
+    import oracle
+    from workloads import WORKLOADS, make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    w_q, w_k, pos = inp.w_q.double().numpy(), inp.w_k.double().numpy(), inp.pos.numpy()
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        q, k, v = (oracle.torch_to_f64(t[sl]) for t in (inp.q, inp.k, inp.v))
+        out = oracle.joint_attention(q, k, v, w_q, w_k, pos)
+        assert np.isfinite(out).all()
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(heads) * w.N * w.N * 128
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(heads)} of {w.B * w.H} (b,h) heads of {name} (N={w.N}), all query rows, "
+                  f"prologue + attention in fp64 NumPy; {dt:.1f} s",
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    main_res = run_gpu(args.workload, args.steps, args.warmup)
+    print(f"bench: {args.workload} forward {main_res['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+    also = None
+    if args.also:
+        r = run_gpu(args.also, args.steps, args.warmup)
+        w = r["workload"]
+        also = {
+            "workload": f"{w.name}: B={w.B} H={w.H} N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128 bf16",
+            "value": round(r["value"], 2),
+            "ms_per_step": round(r["ms_per_step"], 4),
+            "forward_tflops": round(r["forward_tflops"], 2),
+            "forward_frac_of_bf16_peak": round(r["forward_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "prologue_gbs": round(r["prologue_gbs"], 1),
+        }
+        print(f"bench: {args.also} forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        calibrate_copy()
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload, args.cpu_heads)
+
+    w = main_res["workload"]
+    traffic = measured_traffic()
+    line = {
+        "metric": "joint-attention TFLOP/s and % MFMA peak at N=4608 and N=16896, 1 GPU",
+        "value": round(main_res["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v, norm weights 1+0.1*N(0,1), FLUX (t,h,w) position ids",
+        "config": {
+            "workload": f"{w.name}: 2048x2048 text-to-image with CFG, B={w.B} H={w.H} "
+                        f"N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128, prologue + attention",
+            "B": w.B, "H": w.H, "N": w.N, "head_dim": 128,
+        },
+        "roofline": {
+            "kernel": "attn_fwd_kernel (bf16)",
+            "bound": "mfma",
+            "achieved": round(main_res["forward_tflops"], 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_res["forward_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "launch_ms": round(main_res["forward_ms"], 4),
+        },
+        "prologue": {
+            "kernel": "prologue_bf16_kernel",
+            "bound": "hbm",
+            "achieved": round(main_res["prologue_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(main_res["prologue_gbs"] / HBM_PEAK_GBS, 4),
+            "launch_us": round(main_res["prologue_us"], 2),
+        },
+        "also": also,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
