@@ -104,46 +104,84 @@ __device__ __forceinline__ u32x4_t load8(__amdgpu_buffer_rsrc_t r, uint32_t elem
   }
 }
 
-// LDS layouts.  K tile: row = key, 16 chunks of 16 bytes, chunk XOR (key & 15)
-// (ds_read_b128 of 16 consecutive keys hits 16 distinct bank groups).
-// V tile: row = key, chunk XOR 4*(key & 3) (the transposing reads touch 4
-// rows x 4 chunks per 32 lanes).
+// LDS layouts (per stage: K tile then V^T tile, 16 KiB each).
+//  K tile : row = key (256 B), 16-byte chunk c of the head dim stored at
+//           c ^ (key & 15): the 16 keys one ds_read_b128 phase touches hit 16
+//           distinct bank groups.
+//  V^T tile: row = head dim d (128 B = 64 keys), keys permuted inside every
+//           group of 16 (bits 2 and 3 swapped) so that the 8 keys a lane
+//           feeds one PV MFMA are consecutive; chunk c stored at
+//           c ^ ((d >> 1) & 7).
 __device__ __forceinline__ int k_off(int key, int ch) { return key * 256 + ((ch ^ (key & 15)) << 4); }
-__device__ __forceinline__ int v_off(int key, int ch) { return key * 256 + ((ch ^ ((key & 3) << 2)) << 4); }
+__device__ __forceinline__ int vt_off(int d, int ch) { return d * 128 + ((ch ^ ((d >> 1) & 7)) << 4); }
+__device__ __forceinline__ int vperm(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
-// Transposing LDS read: in each group of 16 lanes, lane i receives element
-// i % 4 of the 8-byte loads of lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12.
-__device__ __forceinline__ i16x4_t lds_read_tr(const char *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(__attribute__((address_space(3))) const char *)p);
-}
-
+// Loader of one thread's share of a tile (4 chunks of 16 bytes, as bf16).
+//  K (group 0): chunk idx = rank + 256 i -> key idx / 16, head-dim chunk idx % 16
+//  V (group 1): keys 4 kg .. 4 kg + 3 (kg = rank % 16) of head-dim chunk
+//               dc = rank / 16, transposed into 8 V^T rows on store
 template <bool FP8>
 struct Loader {
-  // This thread's 4 chunks of one tile (group 0: K tile, group 1: V tile).
   u32x4_t r[4];
 
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t src, int tile, int rank) {
+  __device__ __forceinline__ void fetch_k(__amdgpu_buffer_rsrc_t src, int tile, int rank) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = rank + 256 * i;            // 0..1023 chunk of the tile
+      const int idx = rank + 256 * i;
       const int key = tile * kBC + (idx >> 4);
       r[i] = load8<FP8>(src, (uint32_t)key * kHeadDim + 8 * (idx & 15));
     }
   }
-  __device__ __forceinline__ void store(char *tile_base, bool is_v, int rank) const {
+  __device__ __forceinline__ void store_k(char *kt, int rank) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = rank + 256 * i;
-      const int key = idx >> 4, ch = idx & 15;
-      const int off = is_v ? v_off(key, ch) : k_off(key, ch);
-      *reinterpret_cast<u32x4_t *>(tile_base + off) = r[i];
+      *reinterpret_cast<u32x4_t *>(kt + k_off(idx >> 4, idx & 15)) = r[i];
+    }
+  }
+  __device__ __forceinline__ void fetch_v(__amdgpu_buffer_rsrc_t src, int tile, int rank) {
+    const int kg = rank & 15, dc = rank >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = tile * kBC + 4 * kg + i;
+      r[i] = load8<FP8>(src, (uint32_t)key * kHeadDim + 8 * dc);
+    }
+  }
+  __device__ __forceinline__ void store_v(char *vt, int rank) const {
+    const int kg = rank & 15, dc = rank >> 4;
+    const int kp = vperm(4 * kg);   // multiple of 4: the 4 keys stay adjacent
+    const int ch = kp >> 3, within = (kp & 7) * 2;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+      const int w = jj >> 1;
+      u32x2_t out;
+      out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
+      out[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
+      const int d = 8 * dc + jj;
+      *reinterpret_cast<u32x2_t *>(vt + vt_off(d, ch) + within) = out;
     }
   }
 };
+
+// K tile straight from global memory into LDS (bf16 only): group wave gw
+// (0..3) copies 4 KiB = rows 16 gw .. 16 gw + 15; lane l of copy i lands at
+// byte 16 l of its 1 KiB slice, so it fetches the chunk the swizzle puts there.
+__device__ __forceinline__ void k_tile_direct(__amdgpu_buffer_rsrc_t src, char *kt, int tile, int gw, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * gw + 4 * i + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    const uint32_t byte = ((uint32_t)(tile * kBC + row) * kHeadDim + 8 * ch) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) char *)(kt + 1024 * (4 * gw + i)),
+        16, byte, 0, 0, 0);
+  }
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
@@ -164,8 +202,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) order += (simd_of_wave[w] * kWaves + w) < mine;
   }
+  // the sort key is the same in every lane of a wave: keep it scalar
+  order = __builtin_amdgcn_readfirstlane(order);
   const int group = order & 1;
-  const int rank = (order >> 1) * 64 + lane;   // 0..255 inside the group
+  const int gw = order >> 1;                   // wave index inside the group
+  const int rank = gw * 64 + lane;             // 0..255 inside the group
 
   // ---- blockIdx -> (b*h, query tile), consecutive tiles per XCD
   const int ntiles = (N + kBR - 1) / kBR;
@@ -194,19 +235,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   }
 
   const int T = (N + kBC - 1) / kBC;
+  auto k_tile = [&](int j) { return lds + (j % kStages) * kStageBytes; };
+  auto v_tile = [&](int j) { return lds + (j % kStages) * kStageBytes + kKTileBytes; };
 
-  // ---- fill the first stages (all threads: group 0 K, group 1 V); all the
-  // fetches are in flight before the first store waits for its data
+  // ---- prologue of the K/V ring: tiles 0 and 1 in LDS, V tile 2 in flight
   Loader<FP8> ld;
-  const __amdgpu_buffer_rsrc_t my_src = group ? rv : rk;
-  {
-    Loader<FP8> pre[kStages];
-#pragma unroll
-    for (int j = 0; j < kStages; ++j)
-      if (j < T) pre[j].fetch(my_src, j, rank);
-#pragma unroll
-    for (int j = 0; j < kStages; ++j)
-      if (j < T) pre[j].store(lds + j * kStageBytes + group * kKTileBytes, group == 1, rank);
+  if (group == 0) {
+    for (int j = 0; j < 2 && j < T; ++j) {
+      if constexpr (FP8) {
+        ld.fetch_k(rk, j, rank);
+        ld.store_k(k_tile(j), rank);
+      } else {
+        k_tile_direct(rk, k_tile(j), j, gw, lane);
+      }
+    }
+    if constexpr (!FP8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (FP8) {
+      if (2 < T) ld.fetch_k(rk, 2, rank);
+    }
+  } else {
+    for (int j = 0; j < 2 && j < T; ++j) {
+      ld.fetch_v(rv, j, rank);
+      ld.store_v(v_tile(j), rank);
+    }
+    if (2 < T) ld.fetch_v(rv, 2, rank);
   }
 
   // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
@@ -223,116 +275,172 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   f32x16_t s[2];
   bf16x8_t pf[4];
-  float m_run = -INFINITY, l_run = 0.f;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float m_run = -INFINITY;
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // V^T operand addressing (transposing reads): lane = 16 G + j
-  const int G = lane >> 4, j16 = lane & 15;
-  const int v_key_lane = 4 * (G >> 1) + (j16 >> 2);           // + 16 st (+ 8)
-  const int v_byte_lane = 32 * (G & 1) + 8 * (j16 & 3);         // + 64 db
+  // Matrix half-step as a 32-step software pipeline over operand fragments:
+  // steps 0..15 are QK^T of tile jq (kk = s/2, 32-key block kb = s%2), steps
+  // 16..31 PV of tile jv (16-key step st = (s-16)/4, head-dim block
+  // db = (s-16)%4).  Fragment s+kPre is requested from LDS before MFMA s is
+  // issued, and scheduling fences keep that order.
+#ifndef FLUXATTN_PREFETCH
+#define FLUXATTN_PREFETCH 6
+#endif
+  constexpr int kPre = FLUXATTN_PREFETCH;
+  auto frag = [&](int step, const char *ks, const char *vs) -> bf16x8_t {
+    if (step < 16) {
+      const int kk = step >> 1, kb = step & 1;
+      return lds_read_b128(ks + k_off(32 * kb + l32, 2 * kk + hi));
+    }
+    const int st = (step - 16) >> 2, db = (step - 16) & 3;
+    return lds_read_b128(vs + vt_off(32 * db + l32, 2 * st + hi));
+  };
+  auto matrix_step = [&](int step, bf16x8_t f) {
+    if (step < 16) {
+      const int kk = step >> 1, kb = step & 1;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], s[kb], 0, 0, 0);
+    } else {
+      const int st = (step - 16) >> 2, db = (step - 16) & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
+    }
+  };
+  auto matrix_half = [&](int jq, int jv) {
+    const char *ks = k_tile(jq);
+    const char *vs = v_tile(jv);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    bf16x8_t ring[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) ring[i] = frag(i, ks, vs);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const bf16x8_t f = ring[step % kPre];
+      if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, ks, vs);
+      matrix_step(step, f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto qk_only = [&](int j) {
+    const char *ks = k_tile(j);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+    for (int step = 0; step < 16; ++step) matrix_step(step, frag(step, ks, ks));
+  };
+
+  // Online softmax of tile j.  Lane owns query l32 and keys
+  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]).
+  // Short dependency chains: 4 independent max chains, 4 running sums.
+  auto softmax = [&](int j) {
+    if (j * kBC + kBC > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N) s[kb][r] = -INFINITY;
+        }
+    }
+    float mq[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kb = g >> 1, r0 = 8 * (g & 1);
+      float m = fmaxf(s[kb][r0], s[kb][r0 + 1]);
+#pragma unroll
+      for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
+      mq[g] = m;
+    }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+      mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
+    }
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > 8.0f) != 0) {
+      const float alpha = exp2f((m_run - m_new) * c);
+      m_run = m_new;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) l_part[g] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float mc = m_run * c;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, r0 = 8 * (st & 1);
+      bf16x8_t pv8;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c, -mc));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i + 1], c, -mc));
+        l_part[st] += e0 + e1;
+        pv8[i] = (__bf16)e0;
+        pv8[i + 1] = (__bf16)e1;
+      }
+      pf[st] = pv8;
+    }
+    // keep the exponentials in this (vector) half-step: without these the
+    // compiler sinks them next to their MFMA consumers in the matrix one
+#pragma unroll
+    for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(pf[st]));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(l_part[g]));
+  };
 
   __syncthreads();
 
-  // Phase p: group 0 runs half-step h = p, group 1 runs h = p - 1.
-  //   h even: QK^T of tile h/2 (if any) and PV of tile h/2 - 1 (if any)
-  //   h odd : softmax of tile (h-1)/2; store K/V tile (h+3)/2 and fetch the next
-  const int n_phases = 2 * T + 2;
-  for (int p = 0; p < n_phases; ++p) {
-    const int h = p - group;
-    if (h >= 0 && (h & 1) == 0) {
-      const int jq = h >> 1, jv = jq - 1;
-      if (jq < T) {
-        const char *ks = lds + (jq % kStages) * kStageBytes;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8_t kf = lds_read_b128(ks + k_off(32 * kb + l32, 2 * kk + hi));
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
-          }
-        }
+  // Half-steps of every wave, each followed by a workgroup barrier:
+  //   QK(0) | SM(0)+ring | QK(1)+PV(0) | SM(1)+ring | ... | QK+PV(T-1)
+  // Group 1 runs one barrier behind group 0, so in every phase one group is
+  // in a matrix half-step and the other in a vector half-step.
+  // K/V ring (4 stages; tiles j-1 .. j+2 resident during iteration j):
+  //   group 0, vector half-step j: wait for its K tile j+1 copies, start the
+  //     K tile j+2 copies (direct to LDS; fp8: store j+2, fetch j+3);
+  //   group 1, vector half-step j: store V^T tile j+2 (fetched one iteration
+  //     earlier), fetch V tile j+3.
+  // The stage of tile j+2 last held tile j-2, whose PV half-steps (phases
+  // 2j-2 and 2j-1) are over before either group's vector half-step of
+  // iteration j (phases 2j+1 and 2j+2).
+  if (group == 1) __syncthreads();
+  qk_only(0);
+  __syncthreads();
+  for (int j = 0; j < T; ++j) {
+    softmax(j);
+    if (group == 0) {
+      if constexpr (FP8) {
+        if (j + 2 < T) ld.store_k(k_tile(j + 2), rank);
+        if (j + 3 < T) ld.fetch_k(rk, j + 3, rank);
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (j + 2 < T) k_tile_direct(rk, k_tile(j + 2), j + 2, gw, lane);
       }
-      if (jv >= 0 && jv < T) {
-        const char *vs = lds + (jv % kStages) * kStageBytes + kKTileBytes;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int key = 16 * st + v_key_lane;
-            const int byte = 64 * db + v_byte_lane;
-            const int ch = byte >> 4, within = byte & 15;
-            const i16x4_t lo = lds_read_tr(vs + v_off(key, ch) + within);
-            const i16x4_t hi4 = lds_read_tr(vs + v_off(key + 8, ch) + within);
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[db], 0, 0, 0);
-          }
-        }
-      }
-    } else if (h >= 0) {
-      const int js = (h - 1) >> 1;
-      if (js < T) {
-        // ---- online softmax of tile js; lane owns query l32 and keys
-        // 32 kb + 8 (r / 4) + 4 hi + r % 4
-        if (js * kBC + kBC > N) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = js * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key >= N) s[kb][r] = -INFINITY;
-            }
-        }
-        float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > 8.0f) != 0) {
-          const float alpha = exp2f((m_run - m_new) * c);
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        }
-        const float mc = m_run * c;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kb = st >> 1, r0 = 8 * (st & 1);
-          bf16x8_t pv;
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c, -mc));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i + 1], c, -mc));
-            bf16x2_t pr;
-            pr[0] = (__bf16)e0;
-            pr[1] = (__bf16)e1;
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-            pv[i] = pr[0];
-            pv[i + 1] = pr[1];
-          }
-          pf[st] = pv;
-        }
-      }
-      // ---- K/V ring: store tile (h+3)/2 fetched two phases ago, fetch the next
-      const int jw = (h + 3) >> 1;
-      if (jw >= kStages && jw < T) ld.store(lds + (jw % kStages) * kStageBytes + group * kKTileBytes, group == 1, rank);
-      if (jw + 1 >= kStages && jw + 1 < T) ld.fetch(my_src, jw + 1, rank);
+    } else {
+      if (j + 2 < T) ld.store_v(v_tile(j + 2), rank);
+      if (j + 3 < T) ld.fetch_v(rv, j + 3, rank);
     }
     __syncthreads();
+    // one basic block: QK^T of the next tile (recomputed on the last tile
+    // and unused there) followed by PV of this one
+    matrix_half(min(j + 1, T - 1), j);
+    __syncthreads();
   }
+  if (group == 0) __syncthreads();
 
   // ---- epilogue: O / l, one bf16 rounding; lane holds query l32 and head
   // dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end are dropped
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = o_scale / l_tot;
+  float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
+    l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
+  }
+  const float inv = o_scale / l_run;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(a.o) + (size_t)bh * head_elems * 2,
                                               (uint32_t)(head_elems * 2));
 #pragma unroll
