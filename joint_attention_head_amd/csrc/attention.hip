@@ -49,11 +49,11 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;                  // query rows per workgroup
 constexpr int kBC = 64;                           // keys per tile
-constexpr int kStages = 4;
+constexpr int kSlots = 4;                         // per ring (K and V^T)
 constexpr int kKTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = key
-constexpr int kVTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = key
-constexpr int kStageBytes = kKTileBytes + kVTileBytes;
-constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
+constexpr int kVTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = head dim
+constexpr int kVRingOffset = kSlots * kKTileBytes;
+constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 128 KiB
 constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw buffer, 32-bit data format
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -63,6 +63,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -120,67 +122,101 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
-// Loader of one thread's share of a tile (4 chunks of 16 bytes, as bf16).
-//  K (group 0): chunk idx = rank + 256 i -> key idx / 16, head-dim chunk idx % 16
-//  V (group 1): keys 4 kg .. 4 kg + 3 (kg = rank % 16) of head-dim chunk
-//               dc = rank / 16, transposed into 8 V^T rows on store
+// Tile loader.  Each of the two wave groups loads half of every tile:
+// keys [32 g, 32 g + 32) of its K and V^T tiles.
+//  V: thread `rank` of group g owns keys 32 g + 4 kg .. +3 (kg = rank % 8)
+//     at head dims 4 dq .. 4 dq + 3 (dq = rank / 8) and stores them
+//     transposed into 4 V^T rows.
+//  K (fp8 only, bf16 K goes straight to LDS): chunks rank and rank + 256
+//     of the group's 512 16-byte K chunks, widened to bf16.
 template <bool FP8>
 struct Loader {
-  u32x4_t r[4];
+  u32x2_t v[4];
+  u32x4_t k[2];
 
-  __device__ __forceinline__ void fetch_k(__amdgpu_buffer_rsrc_t src, int tile, int rank) {
+  __device__ __forceinline__ void fetch_v(__amdgpu_buffer_rsrc_t src, int tile, int g, int rank) {
+    const int kg = rank & 7, dq = rank >> 3;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = rank + 256 * i;
-      const int key = tile * kBC + (idx >> 4);
-      r[i] = load8<FP8>(src, (uint32_t)key * kHeadDim + 8 * (idx & 15));
+      const uint32_t elem = (uint32_t)(tile * kBC + 32 * g + 4 * kg + i) * kHeadDim + 4 * dq;
+      if constexpr (FP8) {
+        v[i] = e4m3x4_to_bf16x4(__builtin_amdgcn_raw_buffer_load_b32(src, elem, 0, 0));
+      } else {
+        v[i] = __builtin_amdgcn_raw_buffer_load_b64(src, elem * 2, 0, 0);
+      }
     }
   }
-  __device__ __forceinline__ void store_k(char *kt, int rank) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = rank + 256 * i;
-      *reinterpret_cast<u32x4_t *>(kt + k_off(idx >> 4, idx & 15)) = r[i];
-    }
-  }
-  __device__ __forceinline__ void fetch_v(__amdgpu_buffer_rsrc_t src, int tile, int rank) {
-    const int kg = rank & 15, dc = rank >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = tile * kBC + 4 * kg + i;
-      r[i] = load8<FP8>(src, (uint32_t)key * kHeadDim + 8 * dc);
-    }
-  }
-  __device__ __forceinline__ void store_v(char *vt, int rank) const {
-    const int kg = rank & 15, dc = rank >> 4;
-    const int kp = vperm(4 * kg);   // multiple of 4: the 4 keys stay adjacent
+  __device__ __forceinline__ void store_v(char *vt, int g, int rank) const {
+    const int kg = rank & 7, dq = rank >> 3;
+    const int kp = vperm(32 * g + 4 * kg);   // multiple of 4: the 4 keys stay adjacent
     const int ch = kp >> 3, within = (kp & 7) * 2;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = 0; jj < 4; ++jj) {
       const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
       const int w = jj >> 1;
       u32x2_t out;
-      out[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel);
-      out[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel);
-      const int d = 8 * dc + jj;
+      out[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
+      out[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
+      const int d = 4 * dq + jj;
       *reinterpret_cast<u32x2_t *>(vt + vt_off(d, ch) + within) = out;
+    }
+  }
+  __device__ __forceinline__ void fetch_k(__amdgpu_buffer_rsrc_t src, int tile, int g, int rank) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = rank + 256 * i;
+      const int row = 32 * g + (idx >> 4);
+      k[i] = load8<FP8>(src, (uint32_t)(tile * kBC + row) * kHeadDim + 8 * (idx & 15));
+    }
+  }
+  __device__ __forceinline__ void store_k(char *kt, int g, int rank) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = rank + 256 * i;
+      *reinterpret_cast<u32x4_t *>(kt + k_off(32 * g + (idx >> 4), idx & 15)) = k[i];
     }
   }
 };
 
-// K tile straight from global memory into LDS (bf16 only): group wave gw
-// (0..3) copies 4 KiB = rows 16 gw .. 16 gw + 15; lane l of copy i lands at
-// byte 16 l of its 1 KiB slice, so it fetches the chunk the swizzle puts there.
-__device__ __forceinline__ void k_tile_direct(__amdgpu_buffer_rsrc_t src, char *kt, int tile, int gw, int lane) {
+// Raw buffer descriptor words of one head (base, no stride, `bytes`
+// records, 32-bit data format); out-of-range offsets read as zero.
+__device__ __forceinline__ i32x4_t rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = (int)(uint32_t)p;
+  r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = (int)kRsrcWord3;
+  return r;
+}
+
+// Half a K tile straight from global memory into LDS (bf16 only): wave gw
+// (0..3) of group g copies the 2 KiB of rows 32 g + 8 gw .. +8 with two
+// buffer_load_dwordx4 ... lds.  Such a copy writes 16 bytes per lane to
+// LDS [M0 + imm + 16 lane] from global [rsrc + voffset + imm]; both use one
+// M0 and the immediates 0 and 1024.  Lane l of copy i fetches the chunk the
+// K swizzle puts at its LDS slot.  Issued from inline asm so that the
+// compiler does not make every later LDS read wait for it; the kernel orders
+// the copies itself with vmcnt waits before its barriers.
+__device__ __forceinline__ void k_half_direct(i32x4_t rk, uint32_t kt_addr, int tile, int g, int gw, int lane) {
+  const int row0 = 32 * g + 8 * gw;
+  uint32_t vo[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * gw + 4 * i + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int row = row0 + 4 * i + (lane >> 4);
     const int ch = (lane & 15) ^ (row & 15);
     const uint32_t byte = ((uint32_t)(tile * kBC + row) * kHeadDim + 8 * ch) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (__attribute__((address_space(3))) void *)(__attribute__((address_space(3))) char *)(kt + 1024 * (4 * gw + i)),
-        16, byte, 0, 0, 0);
+    vo[i] = byte - 1024u * i;   // row >= 4 i, so byte >= 1024 i
   }
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(kt_addr + 256u * row0);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+      :
+      : "s"(m0), "v"(vo[0]), "v"(vo[1]), "s"(rk)
+      : "memory");
 }
 
 template <bool FP8>
@@ -235,30 +271,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   }
 
   const int T = (N + kBC - 1) / kBC;
-  auto k_tile = [&](int j) { return lds + (j % kStages) * kStageBytes; };
-  auto v_tile = [&](int j) { return lds + (j % kStages) * kStageBytes + kKTileBytes; };
+  auto k_tile = [&](int j) { return lds + (j % kSlots) * kKTileBytes; };
+  auto v_tile = [&](int j) { return lds + kVRingOffset + (j % kSlots) * kVTileBytes; };
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
+  const i32x4_t wk = rsrc_words(kbase, head_bytes);
 
-  // ---- prologue of the K/V ring: tiles 0 and 1 in LDS, V tile 2 in flight
+  // ---- rings.  Both groups load half of every tile.  K runs kKAhead tiles
+  // ahead of its first use (fp8: one tile less, through registers), V^T
+  // two: K tiles 0 .. kKAhead-1 and V^T tiles 0, 1 go in first, V tile 2
+  // (fp8: and K tile 2) is left in flight in the loader registers.
+  constexpr int kKAhead = 3;
   Loader<FP8> ld;
-  if (group == 0) {
-    for (int j = 0; j < 2 && j < T; ++j) {
-      if constexpr (FP8) {
-        ld.fetch_k(rk, j, rank);
-        ld.store_k(k_tile(j), rank);
-      } else {
-        k_tile_direct(rk, k_tile(j), j, gw, lane);
-      }
-    }
-    if constexpr (!FP8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int j = 0; j < 2 && j < T; ++j) {
+    ld.fetch_v(rv, j, group, rank);
+    ld.store_v(v_tile(j), group, rank);
     if constexpr (FP8) {
-      if (2 < T) ld.fetch_k(rk, 2, rank);
+      ld.fetch_k(rk, j, group, rank);
+      ld.store_k(k_tile(j), group, rank);
     }
-  } else {
-    for (int j = 0; j < 2 && j < T; ++j) {
-      ld.fetch_v(rv, j, rank);
-      ld.store_v(v_tile(j), rank);
-    }
-    if (2 < T) ld.fetch_v(rv, 2, rank);
+  }
+  if constexpr (!FP8) {
+    for (int j = 0; j < kKAhead && j < T; ++j)
+      k_half_direct(wk, lds_base + (j % kSlots) * kKTileBytes, j, group, gw, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if (2 < T) {
+    ld.fetch_v(rv, 2, group, rank);
+    if constexpr (FP8) ld.fetch_k(rk, 2, group, rank);
   }
 
   // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
@@ -277,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   bf16x8_t pf[4];
   float m_run = -INFINITY;
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+  const f32x16_t zero = {};
 
   // Matrix half-step as a 32-step software pipeline over operand fragments:
   // steps 0..15 are QK^T of tile jq (kk = s/2, 32-key block kb = s%2), steps
@@ -298,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   auto matrix_step = [&](int step, bf16x8_t f) {
     if (step < 16) {
       const int kk = step >> 1, kb = step & 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], s[kb], 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : zero, 0, 0, 0);
     } else {
       const int st = (step - 16) >> 2, db = (step - 16) & 3;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
@@ -307,10 +347,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   auto matrix_half = [&](int jq, int jv) {
     const char *ks = k_tile(jq);
     const char *vs = v_tile(jv);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
     bf16x8_t ring[kPre];
 #pragma unroll
     for (int i = 0; i < kPre; ++i) ring[i] = frag(i, ks, vs);
@@ -325,10 +361,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   };
   auto qk_only = [&](int j) {
     const char *ks = k_tile(j);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
     for (int step = 0; step < 16; ++step) matrix_step(step, frag(step, ks, ks));
   };
@@ -397,33 +429,37 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   __syncthreads();
 
   // Half-steps of every wave, each followed by a workgroup barrier:
-  //   QK(0) | SM(0)+ring | QK(1)+PV(0) | SM(1)+ring | ... | QK+PV(T-1)
+  //   QK(0) | SM(0)+rings | QK(1)+PV(0) | SM(1)+rings | ... | QK+PV(T-1)
   // Group 1 runs one barrier behind group 0, so in every phase one group is
-  // in a matrix half-step and the other in a vector half-step.
-  // K/V ring (4 stages; tiles j-1 .. j+2 resident during iteration j):
-  //   group 0, vector half-step j: wait for its K tile j+1 copies, start the
-  //     K tile j+2 copies (direct to LDS; fp8: store j+2, fetch j+3);
-  //   group 1, vector half-step j: store V^T tile j+2 (fetched one iteration
-  //     earlier), fetch V tile j+3.
-  // The stage of tile j+2 last held tile j-2, whose PV half-steps (phases
-  // 2j-2 and 2j-1) are over before either group's vector half-step of
-  // iteration j (phases 2j+1 and 2j+2).
+  // in a matrix half-step and the other in a vector half-step.  In its
+  // vector half-step of iteration j each group stores its half of V^T tile
+  // j+2 (fetched one iteration earlier) and fetches its half of tile j+3;
+  // bf16: starts copying its half of K tile j+3 and waits for its K tile j+2
+  // copies; fp8: stores its half of K tile j+2 and fetches tile j+3.  Slot
+  // reuse: the K slot of tile j+3 last held tile j-1, read by QK^T in
+  // iteration j-2; the V^T slot of tile j+2 last held tile j-2, read by PV
+  // in iteration j-2; both are over before either group's vector half-step
+  // of iteration j.
   if (group == 1) __syncthreads();
   qk_only(0);
   __syncthreads();
   for (int j = 0; j < T; ++j) {
     softmax(j);
-    if (group == 0) {
+    if (j + 2 < T) {
+      ld.store_v(v_tile(j + 2), group, rank);
+      if constexpr (FP8) ld.store_k(k_tile(j + 2), group, rank);
+    }
+    if (j + 3 < T) {
+      ld.fetch_v(rv, j + 3, group, rank);
       if constexpr (FP8) {
-        if (j + 2 < T) ld.store_k(k_tile(j + 2), rank);
-        if (j + 3 < T) ld.fetch_k(rk, j + 3, rank);
+        ld.fetch_k(rk, j + 3, group, rank);
       } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (j + 2 < T) k_tile_direct(rk, k_tile(j + 2), j + 2, gw, lane);
+        k_half_direct(wk, lds_base + ((j + 3) % kSlots) * kKTileBytes, j + 3, group, gw, lane);
+        // in flight: this V fetch (4) and this K copy (2); older = K tile j+2
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       }
-    } else {
-      if (j + 2 < T) ld.store_v(v_tile(j + 2), rank);
-      if (j + 3 < T) ld.fetch_v(rv, j + 3, rank);
+    } else if constexpr (!FP8) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
     // one basic block: QK^T of the next tile (recomputed on the last tile
