@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--workload", default="t2i_2048_cfg")
     p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=3, help="(b,h) heads in the CPU oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()

@@ -429,22 +429,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   __syncthreads();
 
   // Half-steps of every wave, each followed by a workgroup barrier:
-  //   QK(0) | SM(0)+rings | QK(1)+PV(0) | SM(1)+rings | ... | QK+PV(T-1)
+  //   QK(0) | SM(0) | rings+QK(1)+PV(0) | SM(1) | ... | rings+QK+PV(T-1)
   // Group 1 runs one barrier behind group 0, so in every phase one group is
-  // in a matrix half-step and the other in a vector half-step.  In its
-  // vector half-step of iteration j each group stores its half of V^T tile
-  // j+2 (fetched one iteration earlier) and fetches its half of tile j+3;
-  // bf16: starts copying its half of K tile j+3 and waits for its K tile j+2
-  // copies; fp8: stores its half of K tile j+2 and fetches tile j+3.  Slot
-  // reuse: the K slot of tile j+3 last held tile j-1, read by QK^T in
-  // iteration j-2; the V^T slot of tile j+2 last held tile j-2, read by PV
-  // in iteration j-2; both are over before either group's vector half-step
-  // of iteration j.
+  // in a matrix half-step and the other in a vector half-step.  A wave
+  // raises its priority for its matrix half-step, so the MFMA stream is
+  // fed first and the softmax of the other wave fills the gaps.
+  // At the start of its matrix half-step of iteration j each group stores
+  // its half of V^T tile j+2 (fetched one iteration earlier) and fetches its
+  // half of tile j+3; bf16: starts copying its half of K tile j+3 and waits
+  // for its K tile j+2 copies (first read in iteration j+1); fp8: stores its
+  // half of K tile j+2 and fetches tile j+3.  Slot reuse: the K slot of
+  // tile j+3 (j+2 for fp8) last held tile j-1 (j-2), read by QK^T in
+  // iteration j-2 (j-3); the V^T slot of tile j+2 last held tile j-2, read
+  // by PV in iteration j-2; the barriers between put those reads before
+  // either group's matrix half-step of iteration j.
   if (group == 1) __syncthreads();
   qk_only(0);
   __syncthreads();
   for (int j = 0; j < T; ++j) {
     softmax(j);
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(3);
     if (j + 2 < T) {
       ld.store_v(v_tile(j + 2), group, rank);
       if constexpr (FP8) ld.store_k(k_tile(j + 2), group, rank);
@@ -455,16 +460,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
         ld.fetch_k(rk, j + 3, group, rank);
       } else {
         k_half_direct(wk, lds_base + ((j + 3) % kSlots) * kKTileBytes, j + 3, group, gw, lane);
-        // in flight: this V fetch (4) and this K copy (2); older = K tile j+2
         asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       }
     } else if constexpr (!FP8) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();
-    // one basic block: QK^T of the next tile (recomputed on the last tile
-    // and unused there) followed by PV of this one
     matrix_half(min(j + 1, T - 1), j);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
   if (group == 0) __syncthreads();
