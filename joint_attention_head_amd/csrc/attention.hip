@@ -16,22 +16,28 @@
 //  * O^T = V^T P^T takes the probabilities straight from registers as the B
 //    operand.  The keys a lane holds for one MFMA step are
 //    {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); since keys are summed over,
-//    the V^T operand only has to list the same keys in the same order, which
-//    two ds_read_b64_tr_b16 transposing reads of the row-major V tile do.
+//    the V^T operand only has to list the same keys in the same order.  V
+//    tiles are stored transposed in LDS (row = head dim) with bits 2 and 3
+//    of the key swapped inside every group of 16, so that list is one
+//    ds_read_b128 per lane.
 //  * Ping-pong: the waves form two groups of four, one wave of each group per
 //    SIMD.  Every phase ends with a workgroup barrier; in each phase one
 //    group runs its matrix half-step (QK^T of the next tile, PV of the
-//    current one: 32 MFMAs) while the other runs its vector half-step (online
-//    softmax of the next tile, plus its share of the K/V tile loads), so the
-//    matrix cores and the VALU of every SIMD are busy at the same time.
-//  * K/V tiles of 64 keys go through a 4-stage LDS ring (128 KiB).  Group 0
-//    loads K tiles and group 1 V tiles, global -> VGPR in one vector
-//    half-step and VGPR -> LDS two phases later.  Buffer-resource loads
-//    return 0 past the end of a head, so ragged tails need no branches.
+//    current one: 32 MFMAs, at raised wave priority) while the other runs
+//    its vector half-step (online softmax of the next tile), so the matrix
+//    cores and the VALU of every SIMD are busy at the same time.
+//  * K tiles and V^T tiles of 64 keys go through two 4-slot LDS rings
+//    (64 KiB each).  Both groups load half of every tile at the start of
+//    their matrix half-steps: bf16 K by direct global -> LDS buffer loads,
+//    three tiles ahead; V (and fp8 K) global -> VGPR one iteration before
+//    the transposing VGPR -> LDS store, two tiles ahead.  Buffer-resource
+//    loads return 0 past the end of a head, so ragged tails need no
+//    branches; the softmax masks keys >= N.
 //  * Online softmax in base 2 (scale * log2 e folded into one FMA).  The
 //    running max only moves, and O and l are rescaled, when a row's max grows
 //    by more than 8 (log2 units); probabilities stay <= 2^8 and O / l is
-//    unchanged.  l sums the bf16-rounded probabilities the MFMA consumes.
+//    unchanged.  l sums the fp32 probabilities; P is rounded to bf16 for
+//    the MFMA.
 //  * blockIdx is remapped so that the workgroups the dispatcher sends to one
 //    XCD (blockIdx % 8) take consecutive query tiles of the same (b,h) and
 //    share its K/V stream through that XCD's L2.
