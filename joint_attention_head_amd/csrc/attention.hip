@@ -22,26 +22,35 @@
 //    ds_read_b128 per lane.
 //  * Ping-pong: the waves form two groups of four, one wave of each group per
 //    SIMD.  Every phase ends with a workgroup barrier; in each phase one
-//    group runs its matrix half-step (QK^T of the next tile, PV of the
-//    current one: 32 MFMAs, at raised wave priority) while the other runs
-//    its vector half-step (online softmax of the next tile), so the matrix
-//    cores and the VALU of every SIMD are busy at the same time.
+//    group runs its matrix half-step (PV of the current tile, QK^T of the
+//    next one: 32 MFMAs, at raised wave priority) while the other runs its
+//    vector half-step (online softmax of the next tile), so the matrix cores
+//    and the VALU of every SIMD are busy at the same time.
+//  * The matrix half-step issues no VALU instruction: a VALU op of the MFMA
+//    wave would queue behind the other wave's softmax and hold up the MFMA
+//    stream.  LDS addresses are lane constants plus immediates (the loop is
+//    unrolled over the four ring slots), global loads take per-tile buffer
+//    descriptors built with scalar ops, and the V transpose permutes run in
+//    the vector half-step.
 //  * K tiles and V^T tiles of 64 keys go through two 4-slot LDS rings
-//    (64 KiB each).  Both groups load half of every tile at the start of
-//    their matrix half-steps: bf16 K by direct global -> LDS buffer loads,
-//    three tiles ahead; V (and fp8 K) global -> VGPR one iteration before
-//    the transposing VGPR -> LDS store, two tiles ahead.  Buffer-resource
-//    loads return 0 past the end of a head, so ragged tails need no
-//    branches; the softmax masks keys >= N.
-//  * Online softmax in base 2 (scale * log2 e folded into one FMA).  The
-//    running max only moves, and O and l are rescaled, when a row's max grows
-//    by more than 8 (log2 units); probabilities stay <= 2^8 and O / l is
-//    unchanged.  l sums the fp32 probabilities; P is rounded to bf16 for
-//    the MFMA.
+//    (64 KiB each).  Both groups load half of every tile, spread over their
+//    matrix half-steps: bf16 K by direct global -> LDS buffer loads, three
+//    tiles ahead; V (and fp8 K) global -> VGPR, permuted (widened) in the
+//    next vector half-step and written to LDS in the matrix half-step after
+//    that, two tiles ahead.  Buffer-resource loads return 0 past the end of a
+//    head, so ragged tails need no branches; the softmax masks keys >= N.
+//  * Online softmax in base 2 with no arithmetic besides the exponentials:
+//    Q is pre-multiplied by scale * log2 e, and QK^T starts accumulating at
+//    minus the row's running shift b, so the MFMA delivers c*S - b.  The
+//    row maximum is only scanned when the tile's row sum (an upper bound of
+//    every probability in it) exceeds 2^16; b then moves up to the maximum
+//    if that exceeds it by more than 8, with O and l rescaled.  O / l is
+//    unchanged by the shift.  l sums the fp32 probabilities; P is rounded
+//    to bf16 for the MFMA.
 //  * blockIdx is remapped so that the workgroups the dispatcher sends to one
 //    XCD (blockIdx % 8) take consecutive query tiles of the same (b,h) and
 //    share its K/V stream through that XCD's L2.
-//  * fp8 (OCP E4M3) inputs are widened to bf16 on load, which is exact; the
+//  * fp8 (OCP E4M3) inputs are widened to bf16, which is exact; the
 //    per-(b,h) scales are folded into the softmax scale (q, k) and into the
 //    final normalisation (v).
 #include "fluxattn_internal.h"
@@ -64,14 +73,17 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw buffer, 32-bit data for
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <int R>
+struct Slot {
+  static constexpr int value = R;
+};
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v;
@@ -90,29 +102,33 @@ __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(u32x2_t w) {
+  const u32x2_t a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+  u32x4_t v;
+  v[0] = a[0];
+  v[1] = a[1];
+  v[2] = b[0];
+  v[3] = b[1];
+  return v;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
-// 8 consecutive head-dim elements (element offset `elem` inside one head),
-// widened to bf16; reads past the head's end return zeros.
-template <bool FP8>
-__device__ __forceinline__ u32x4_t load8(__amdgpu_buffer_rsrc_t r, uint32_t elem) {
-  if constexpr (FP8) {
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, elem, 0, 0);
-    const u32x2_t a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-    u32x4_t v;
-    v[0] = a[0];
-    v[1] = a[1];
-    v[2] = b[0];
-    v[3] = b[1];
-    return v;
-  } else {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0);
-  }
+// Raw buffer descriptor words (base, no stride, `bytes` records, 32-bit
+// data format); out-of-range offsets read as zero.
+__device__ __forceinline__ i32x4_t rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = (int)(uint32_t)p;
+  r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = (int)kRsrcWord3;
+  return r;
 }
 
-// LDS layouts (per stage: K tile then V^T tile, 16 KiB each).
+// LDS layouts (K ring, then V^T ring; 16 KiB per slot).
 //  K tile : row = key (256 B), 16-byte chunk c of the head dim stored at
 //           c ^ (key & 15): the 16 keys one ds_read_b128 phase touches hit 16
 //           distinct bank groups.
@@ -126,103 +142,6 @@ __device__ __forceinline__ int vperm(int key) { return (key & ~12) | ((key & 4) 
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
-}
-
-// Tile loader.  Each of the two wave groups loads half of every tile:
-// keys [32 g, 32 g + 32) of its K and V^T tiles.
-//  V: thread `rank` of group g owns keys 32 g + 4 kg .. +3 (kg = rank % 8)
-//     at head dims 4 dq .. 4 dq + 3 (dq = rank / 8) and stores them
-//     transposed into 4 V^T rows.
-//  K (fp8 only, bf16 K goes straight to LDS): chunks rank and rank + 256
-//     of the group's 512 16-byte K chunks, widened to bf16.
-template <bool FP8>
-struct Loader {
-  u32x2_t v[4];
-  u32x4_t k[2];
-
-  __device__ __forceinline__ void fetch_v(__amdgpu_buffer_rsrc_t src, int tile, int g, int rank) {
-    const int kg = rank & 7, dq = rank >> 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t elem = (uint32_t)(tile * kBC + 32 * g + 4 * kg + i) * kHeadDim + 4 * dq;
-      if constexpr (FP8) {
-        v[i] = e4m3x4_to_bf16x4(__builtin_amdgcn_raw_buffer_load_b32(src, elem, 0, 0));
-      } else {
-        v[i] = __builtin_amdgcn_raw_buffer_load_b64(src, elem * 2, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_v(char *vt, int g, int rank) const {
-    const int kg = rank & 7, dq = rank >> 3;
-    const int kp = vperm(32 * g + 4 * kg);   // multiple of 4: the 4 keys stay adjacent
-    const int ch = kp >> 3, within = (kp & 7) * 2;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      const int w = jj >> 1;
-      u32x2_t out;
-      out[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);
-      out[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);
-      const int d = 4 * dq + jj;
-      *reinterpret_cast<u32x2_t *>(vt + vt_off(d, ch) + within) = out;
-    }
-  }
-  __device__ __forceinline__ void fetch_k(__amdgpu_buffer_rsrc_t src, int tile, int g, int rank) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = rank + 256 * i;
-      const int row = 32 * g + (idx >> 4);
-      k[i] = load8<FP8>(src, (uint32_t)(tile * kBC + row) * kHeadDim + 8 * (idx & 15));
-    }
-  }
-  __device__ __forceinline__ void store_k(char *kt, int g, int rank) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = rank + 256 * i;
-      *reinterpret_cast<u32x4_t *>(kt + k_off(32 * g + (idx >> 4), idx & 15)) = k[i];
-    }
-  }
-};
-
-// Raw buffer descriptor words of one head (base, no stride, `bytes`
-// records, 32-bit data format); out-of-range offsets read as zero.
-__device__ __forceinline__ i32x4_t rsrc_words(const void *base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = (int)(uint32_t)p;
-  r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
-  r[2] = (int)bytes;
-  r[3] = (int)kRsrcWord3;
-  return r;
-}
-
-// Half a K tile straight from global memory into LDS (bf16 only): wave gw
-// (0..3) of group g copies the 2 KiB of rows 32 g + 8 gw .. +8 with two
-// buffer_load_dwordx4 ... lds.  Such a copy writes 16 bytes per lane to
-// LDS [M0 + imm + 16 lane] from global [rsrc + voffset + imm]; both use one
-// M0 and the immediates 0 and 1024.  Lane l of copy i fetches the chunk the
-// K swizzle puts at its LDS slot.  Issued from inline asm so that the
-// compiler does not make every later LDS read wait for it; the kernel orders
-// the copies itself with vmcnt waits before its barriers.
-__device__ __forceinline__ void k_half_direct(i32x4_t rk, uint32_t kt_addr, int tile, int g, int gw, int lane) {
-  const int row0 = 32 * g + 8 * gw;
-  uint32_t vo[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = row0 + 4 * i + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
-    const uint32_t byte = ((uint32_t)(tile * kBC + row) * kHeadDim + 8 * ch) * 2;
-    vo[i] = byte - 1024u * i;   // row >= 4 i, so byte >= 1024 i
-  }
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(kt_addr + 256u * row0);
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
-      :
-      : "s"(m0), "v"(vo[0]), "v"(vo[1]), "s"(rk)
-      : "memory");
 }
 
 template <bool FP8>
@@ -260,14 +179,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const int qt = logical - bh * ntiles;
 
   constexpr int kElem = FP8 ? 1 : 2;
+  constexpr uint32_t kTileGlobal = kBC * kHeadDim * kElem;   // bytes of one K/V tile in HBM
   const size_t head_elems = (size_t)N * kHeadDim;
   const uint32_t head_bytes = (uint32_t)(head_elems * kElem);
   const char *qbase = static_cast<const char *>(a.q) + (size_t)bh * head_elems * kElem;
   const char *kbase = static_cast<const char *>(a.k) + (size_t)bh * head_elems * kElem;
   const char *vbase = static_cast<const char *>(a.v) + (size_t)bh * head_elems * kElem;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, head_bytes);
 
   float c = a.scale_log2;
   float o_scale = 1.f;
@@ -275,43 +192,181 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     c *= a.q_scale[bh] * a.k_scale[bh];
     o_scale = a.v_scale[bh];
   }
-
   const int T = (N + kBC - 1) / kBC;
-  auto k_tile = [&](int j) { return lds + (j % kSlots) * kKTileBytes; };
-  auto v_tile = [&](int j) { return lds + kVRingOffset + (j % kSlots) * kVTileBytes; };
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
-  const i32x4_t wk = rsrc_words(kbase, head_bytes);
 
-  // ---- rings.  Both groups load half of every tile.  K runs kKAhead tiles
-  // ahead of its first use (fp8: one tile less, through registers), V^T
-  // two: K tiles 0 .. kKAhead-1 and V^T tiles 0, 1 go in first, V tile 2
-  // (fp8: and K tile 2) is left in flight in the loader registers.
-  constexpr int kKAhead = 3;
-  Loader<FP8> ld;
-  for (int j = 0; j < 2 && j < T; ++j) {
-    ld.fetch_v(rv, j, group, rank);
-    ld.store_v(v_tile(j), group, rank);
+  // ---- per-tile buffer descriptors: base moved to the tile, records cut
+  // to what is left of the head, so lane offsets stay tile-independent and
+  // reads past the head's end still return zero.  Scalar arithmetic only.
+  auto tile_rsrc = [&](const char *base, int t) __attribute__((always_inline)) {
+    return make_rsrc(base + (size_t)t * kTileGlobal, head_bytes - (uint32_t)t * kTileGlobal);
+  };
+  auto tile_words = [&](const char *base, int t) __attribute__((always_inline)) {
+    return rsrc_words(base + (size_t)t * kTileGlobal, head_bytes - (uint32_t)t * kTileGlobal);
+  };
+
+  // ---- lane constants (bytes).  Each group loads half of every tile:
+  // keys [32 g, 32 g + 32).
+  //  V: thread `rank` owns keys 32 g + 4 kg .. +3 (kg = rank % 8) at head
+  //     dims 4 dq .. +3 (dq = rank / 8): load i reads key 32 g + 4 kg + i,
+  //     and the transposed 4x4 block goes to V^T rows 4 dq + jj.
+  const int kg = rank & 7, dq = rank >> 3;
+  const uint32_t v_goff = (uint32_t)((32 * group + 4 * kg) * kHeadDim + 4 * dq) * kElem;
+  // (rows 4 dq + 1 and 4 dq + 3 share the swizzle of rows 4 dq and 4 dq + 2
+  // and sit 128 bytes after them)
+  uint32_t v_soff[2];
+  {
+    const int kp = vperm(32 * group + 4 * kg);   // multiple of 4: the 4 keys stay adjacent
+    const int ch = kp >> 3, within = (kp & 7) * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v_soff[h] = (uint32_t)(kVRingOffset + vt_off(4 * dq + 2 * h, ch) + within);
+  }
+  //  fp8 K: chunks rank and rank + 256 of the group's 512 16-byte chunks
+  //     (8 keys per lane-load), widened to bf16 on the way to LDS.
+  const uint32_t k_goff = (uint32_t)((32 * group + (rank >> 4)) * kHeadDim + 8 * (rank & 15)) * kElem;
+  // (chunk rank + 256 is 16 keys further: same swizzle, 4 KiB on)
+  const uint32_t k_soff = (uint32_t)k_off(32 * group + (rank >> 4), rank & 15);
+  //  bf16 K by direct copies: wave gw of group g copies rows
+  //     32 g + 8 gw .. +8 with two buffer_load_dwordx4 ... lds; lane l of
+  //     copy i fetches the chunk the K swizzle puts at LDS slot row
+  //     32 g + 8 gw + 4 i + l / 16, chunk position l % 16.
+  uint32_t k_dgoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * group + 8 * gw + 4 * i + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    k_dgoff[i] = (uint32_t)(row * kHeadDim + 8 * ch) * 2;
+  }
+  const uint32_t k_m0 = lds_base + 256u * (uint32_t)(32 * group + 8 * gw);
+  //  MFMA fragments: K (kk) row l32, chunk 2 kk + hi; V^T (st) row l32,
+  //     chunk 2 st + hi.  Slot, 32-key block and head-dim block are
+  //     immediates.
+  uint32_t kf[8], vf[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kf[kk] = (uint32_t)k_off(l32, 2 * kk + hi);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) vf[st] = (uint32_t)(kVRingOffset + vt_off(l32, 2 * st + hi));
+
+  // ---- ring traffic helpers
+  u32x2_t vraw[4];        // bf16: 4 keys x 4 dims per lane; fp8: 4 keys x 4 dims in vraw[i][0]
+  u32x2_t kraw[2];        // fp8 K: 8 codes per chunk
+  u32x2_t vt_data[4];     // transposed V rows, ready for LDS
+  u32x4_t kt_data[2];     // fp8 K widened to bf16, ready for LDS
+  auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
     if constexpr (FP8) {
-      ld.fetch_k(rk, j, group, rank);
-      ld.store_k(k_tile(j), group, rank);
+      vraw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(r, v_goff + (uint32_t)(i * kHeadDim * kElem), 0, 0);
+    } else {
+      vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, v_goff + (uint32_t)(i * kHeadDim * kElem), 0, 0);
+    }
+  };
+  auto fetch_k_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
+    kraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, k_goff + (uint32_t)(16 * i * kHeadDim * kElem), 0, 0);
+  };
+  // VGPR -> transposed rows (vector half-step work)
+  auto prepare_v = [&]() __attribute__((always_inline)) {
+    u32x2_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = FP8 ? e4m3x4_to_bf16x4(vraw[i][0]) : vraw[i];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+      const int h = jj >> 1;
+      vt_data[jj][0] = __builtin_amdgcn_perm(w[1][h], w[0][h], sel);
+      vt_data[jj][1] = __builtin_amdgcn_perm(w[3][h], w[2][h], sel);
+    }
+  };
+  auto prepare_k = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kt_data[i] = e4m3x8_to_bf16x8(kraw[i]);
+  };
+  auto store_v = [&](int slot_bytes) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<u32x2_t *>(lds + v_soff[jj >> 1] + (slot_bytes + 128 * (jj & 1))) = vt_data[jj];
+  };
+  auto store_k = [&](int slot_bytes) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t *>(lds + k_soff + (slot_bytes + 4096 * i)) = kt_data[i];
+  };
+  // one of the two direct K copies of this wave (bf16): 1 KiB = 4 rows
+  auto k_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
+    const uint32_t m0 = k_m0 + slot_bytes + 1024u * (uint32_t)i;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(k_dgoff[i]), "s"(words)
+        : "memory");
+  };
+
+  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1 (fp8) or
+  // 0, 1, 2 (bf16 copies) in LDS; V tile 2 and fp8 K tile 2 in registers.
+  for (int j = 0; j < 2 && j < T; ++j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
+    prepare_v();
+    store_v(j * kVTileBytes);
+    if constexpr (FP8) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
+      prepare_k();
+      store_k(j * kKTileBytes);
     }
   }
   if constexpr (!FP8) {
-    for (int j = 0; j < kKAhead && j < T; ++j)
-      k_half_direct(wk, lds_base + (j % kSlots) * kKTileBytes, j, group, gw, lane);
+    for (int j = 0; j < 3 && j < T; ++j) {
+      const i32x4_t w = tile_words(kbase, j);
+      k_dma_one(w, j * kKTileBytes, 0);
+      k_dma_one(w, j * kKTileBytes, 1);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  if (2 < T) {
-    ld.fetch_v(rv, 2, group, rank);
-    if constexpr (FP8) ld.fetch_k(rk, 2, group, rank);
+  {
+    const int t2 = min(2, T - 1);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, t2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
+    if constexpr (FP8) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, t2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
+    }
   }
 
-  // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
+  // ---- queries, pre-multiplied by c = softmax scale * log2(e) (and the
+  // fp8 scales) and rounded to bf16, so that QK^T yields base-2 logits:
+  // qf[kk] = c * Q[q][16kk + 8hi .. +8), q = this lane's row
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8_t, load8<FP8>(rq, (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi));
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t elem = (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi;
+      float x[8];
+      if constexpr (FP8) {
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
+          const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
+          x[4 * h + 0] = lo[0];
+          x[4 * h + 1] = lo[1];
+          x[4 * h + 2] = up[0];
+          x[4 * h + 3] = up[1];
+        }
+      } else {
+        const bf16x8_t v = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)(x[i] * c);
+    }
+  }
 
   f32x16_t o[4];
 #pragma unroll
@@ -320,61 +375,49 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   f32x16_t s[2];
   bf16x8_t pf[4];
-  float m_run = -INFINITY;
+  // QK^T starts its accumulation at -b (b = this row's running shift in
+  // base-2 units), so the scores arrive as c*S - b and the exponentials
+  // need no extra arithmetic
+  float b_run = 0.f;
+  f32x16_t bias = {};
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-  const f32x16_t zero = {};
 
   // Matrix half-step as a 32-step software pipeline over operand fragments:
-  // steps 0..15 are QK^T of tile jq (kk = s/2, 32-key block kb = s%2), steps
-  // 16..31 PV of tile jv (16-key step st = (s-16)/4, head-dim block
-  // db = (s-16)%4).  Fragment s+kPre is requested from LDS before MFMA s is
-  // issued, and scheduling fences keep that order.
-#ifndef FLUXATTN_PREFETCH
-#define FLUXATTN_PREFETCH 6
-#endif
-  constexpr int kPre = FLUXATTN_PREFETCH;
-  auto frag = [&](int step, const char *ks, const char *vs) -> bf16x8_t {
-    if (step < 16) {
-      const int kk = step >> 1, kb = step & 1;
-      return lds_read_b128(ks + k_off(32 * kb + l32, 2 * kk + hi));
+  // steps 0..15 are PV of the current tile (16-key step st = s/4, head-dim
+  // block db = s%4), steps 16..31 QK^T of the next tile (kk = (s-16)/2,
+  // 32-key block kb = (s-16)%2).  Fragment s+kPre is requested from LDS
+  // before MFMA s is issued, and scheduling fences keep that order.  The
+  // V^T tile of the PV steps is complete before the half-step starts, so
+  // the first kPre fragments are requested before the barrier.
+  constexpr int kPre = 6;
+  auto frag = [&](int step, int kslot_bytes, int vslot_bytes) __attribute__((always_inline)) -> bf16x8_t {
+    if (step >= 16) {
+      const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
+      return lds_read_b128(lds + kf[kk] + (kslot_bytes + kb * 32 * 256));
     }
-    const int st = (step - 16) >> 2, db = (step - 16) & 3;
-    return lds_read_b128(vs + vt_off(32 * db + l32, 2 * st + hi));
+    const int st = step >> 2, db = step & 3;
+    return lds_read_b128(lds + vf[st] + (vslot_bytes + db * 32 * 128));
   };
-  auto matrix_step = [&](int step, bf16x8_t f) {
-    if (step < 16) {
-      const int kk = step >> 1, kb = step & 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : zero, 0, 0, 0);
+  auto matrix_step = [&](int step, bf16x8_t f) __attribute__((always_inline)) {
+    if (step >= 16) {
+      const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : bias, 0, 0, 0);
     } else {
-      const int st = (step - 16) >> 2, db = (step - 16) & 3;
+      const int st = step >> 2, db = step & 3;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
     }
   };
-  auto matrix_half = [&](int jq, int jv) {
-    const char *ks = k_tile(jq);
-    const char *vs = v_tile(jv);
-    bf16x8_t ring[kPre];
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) ring[i] = frag(i, ks, vs);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int step = 0; step < 32; ++step) {
-      const bf16x8_t f = ring[step % kPre];
-      if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, ks, vs);
-      matrix_step(step, f);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto qk_only = [&](int j) {
-    const char *ks = k_tile(j);
-#pragma unroll
-    for (int step = 0; step < 16; ++step) matrix_step(step, frag(step, ks, ks));
-  };
 
   // Online softmax of tile j.  Lane owns query l32 and keys
-  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]).
-  // Short dependency chains: 4 independent max chains, 4 running sums.
-  auto softmax = [&](int j) {
+  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]),
+  // as x = c*S - b.  Common case: p = 2^x straight away; the row maximum is
+  // only needed when some p may be large, which the tile's own row sum
+  // (>= every p in it) tells.  Then, or on the first tile, b moves up to the
+  // row maximum when that exceeds it by more than 8 (first tile: moves to
+  // it), O and l are scaled by 2^-shift and p recomputed, so p <= 2^16
+  // always and O / l is unchanged.
+  auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value != 0;
     if (j * kBC + kBC > N) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -384,46 +427,65 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
           if (key >= N) s[kb][r] = -INFINITY;
         }
     }
-    float mq[4];
+    float t[4];
+    auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int kb = g >> 1, r0 = 8 * (g & 1);
-      float m = fmaxf(s[kb][r0], s[kb][r0 + 1]);
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st >> 1, r0 = 8 * (st & 1);
+        float acc = 0.f;
+        bf16x8_t pv8;
 #pragma unroll
-      for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
-      mq[g] = m;
-    }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
-      mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
-    }
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > 8.0f) != 0) {
-      const float alpha = exp2f((m_run - m_new) * c);
-      m_run = m_new;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) l_part[g] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
-    const float mc = m_run * c;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st >> 1, r0 = 8 * (st & 1);
-      bf16x8_t pv8;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c, -mc));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i + 1], c, -mc));
-        l_part[st] += e0 + e1;
-        pv8[i] = (__bf16)e0;
-        pv8[i + 1] = (__bf16)e1;
+        for (int i = 0; i < 8; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(s[kb][r0 + i]);
+          const float e1 = __builtin_amdgcn_exp2f(s[kb][r0 + i + 1]);
+          acc += e0 + e1;
+          pv8[i] = (__bf16)e0;
+          pv8[i + 1] = (__bf16)e1;
+        }
+        t[st] = acc;
+        pf[st] = pv8;
       }
-      pf[st] = pv8;
+    };
+    if constexpr (!kFirst) exps();
+    const float tot = (t[0] + t[1]) + (t[2] + t[3]);
+    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= 65536.f)) != 0) {
+      float mq[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kb = g >> 1, r0 = 8 * (g & 1);
+        float m = fmaxf(s[kb][r0], s[kb][r0 + 1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
+        mq[g] = m;
+      }
+      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+        mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
+      }
+      if (kFirst || __builtin_amdgcn_ballot_w64(mx > 8.0f) != 0) {
+        const float d = kFirst ? mx : fmaxf(mx, 0.f);
+        b_run += d;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bias[i] = -b_run;
+        if constexpr (!kFirst) {
+          const float alpha = __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) l_part[g] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= d;
+        exps();
+      }
     }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) l_part[st] += t[st];
     // keep the exponentials in this (vector) half-step: without these the
     // compiler sinks them next to their MFMA consumers in the matrix one
 #pragma unroll
@@ -432,49 +494,104 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(l_part[g]));
   };
 
-  __syncthreads();
-
-  // Half-steps of every wave, each followed by a workgroup barrier:
-  //   QK(0) | SM(0) | rings+QK(1)+PV(0) | SM(1) | ... | rings+QK+PV(T-1)
+  // Schedule of each wave: QK^T(0), vector half-step of tile 0, then per
+  // tile j a matrix half-step (PV(j), QK^T(j+1)) followed by the vector
+  // half-step of tile j+1 (softmax, V permutes, first PV fragment reads).
   // Group 1 runs one barrier behind group 0, so in every phase one group is
-  // in a matrix half-step and the other in a vector half-step.  A wave
-  // raises its priority for its matrix half-step, so the MFMA stream is
-  // fed first and the softmax of the other wave fills the gaps.
-  // At the start of its matrix half-step of iteration j each group stores
-  // its half of V^T tile j+2 (fetched one iteration earlier) and fetches its
-  // half of tile j+3; bf16: starts copying its half of K tile j+3 and waits
-  // for its K tile j+2 copies (first read in iteration j+1); fp8: stores its
-  // half of K tile j+2 and fetches tile j+3.  Slot reuse: the K slot of
-  // tile j+3 (j+2 for fp8) last held tile j-1 (j-2), read by QK^T in
-  // iteration j-2 (j-3); the V^T slot of tile j+2 last held tile j-2, read
-  // by PV in iteration j-2; the barriers between put those reads before
-  // either group's matrix half-step of iteration j.
-  if (group == 1) __syncthreads();
-  qk_only(0);
-  __syncthreads();
-  for (int j = 0; j < T; ++j) {
-    softmax(j);
-    __syncthreads();
+  // in a matrix half-step and the other in a vector half-step.
+  // Ring traffic of the matrix half-step of tile j: write V^T tile j+2 (fp8:
+  // and K tile j+2, widened there) to LDS, fetch V tile j+3 (fp8: K tile
+  // j+3) into VGPRs, copy bf16 K tile j+3 into LDS.  Slot reuse: the V^T and
+  // fp8 K slot of tile j+2 last held tile j-2, read by PV(j-2) (QK^T(j-2))
+  // in matrix half-step j-2 (j-3); the bf16 K slot of tile j+3 last held
+  // tile j-1, read by QK^T(j-1) in matrix half-step j-2; at least one
+  // barrier separates those reads from either group's writes.  Tile indices
+  // of the fetches are clamped to T-1: extra copies land in slots no later
+  // step reads.  The vmcnt wait in each vector half-step retires the
+  // previous matrix half-step's loads, so a bf16 K copy is in LDS two
+  // barriers before QK^T first reads it.
+  // where in the 32-step matrix pipeline the ring traffic goes: LDS writes
+  // of tile j+2, the four V loads of tile j+3, the two K copies (or loads)
+  constexpr int kStoreStep = 10, kVLoad0 = 12, kVLoadGap = 4, kKLoad0 = 26, kKLoadGap = 3;
+  // vector half-step tail: permute (fp8: widen) the V (K) tile fetched in
+  // the previous matrix half-step, and request the first PV fragments of
+  // the next matrix half-step (V^T slot of tile j, K slot of tile j+1)
+  auto vector_tail = [&](int kslot_bytes, int vslot_bytes, bf16x8_t *ring) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    prepare_v();
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) ring[i] = frag(i, kslot_bytes, vslot_bytes);
+  };
+  // Iteration j (ring slot R = j % 4): matrix half-step PV(j), QK^T(j+1)
+  // with the ring traffic, then the vector half-step of tile j+1.
+  auto iteration = [&](int j, auto slot, bf16x8_t *ring) __attribute__((always_inline)) {
+    constexpr int R = decltype(slot)::value;
+    constexpr int kCur = R * kKTileBytes;                       // V^T slot of tile j (same byte offset in both rings)
+    constexpr int kNext = ((R + 1) % kSlots) * kKTileBytes;    // slots of tile j+1
+    constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // slots of tile j+2
+    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
+    const int tn = min(j + 3, T - 1);
+    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vbase, tn);
+    // the vector half-step wrote no LDS, and the fragment reads it issued
+    // touch a slot no wave writes before the next barrier: a plain barrier
+    // that does not wait for them
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(3);
-    if (j + 2 < T) {
-      ld.store_v(v_tile(j + 2), group, rank);
-      if constexpr (FP8) ld.store_k(k_tile(j + 2), group, rank);
-    }
-    if (j + 3 < T) {
-      ld.fetch_v(rv, j + 3, group, rank);
-      if constexpr (FP8) {
-        ld.fetch_k(rk, j + 3, group, rank);
-      } else {
-        k_half_direct(wk, lds_base + ((j + 3) % kSlots) * kKTileBytes, j + 3, group, gw, lane);
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      const bf16x8_t f = ring[step % kPre];
+      if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, kNext, kCur);
+      matrix_step(step, f);
+      if (step == kStoreStep) {
+        store_v(kPlus2);
+        if constexpr (FP8) {
+          // widened here rather than in the vector half-step: keeps 8 VGPRs
+          // free across the barrier, at the cost of 16 VALU ops (fp8 only)
+          prepare_k();
+          store_k(kPlus2);
+        }
       }
-    } else if constexpr (!FP8) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (step >= kVLoad0 && step < kVLoad0 + 4 * kVLoadGap && (step - kVLoad0) % kVLoadGap == 0)
+        fetch_v_one(rvn, (step - kVLoad0) / kVLoadGap);
+      if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) {
+        const int i = step == kKLoad0 ? 0 : 1;
+        if constexpr (FP8) {
+          fetch_k_one(tile_rsrc(kbase, tn), i);
+        } else {
+          k_dma_one(tile_words(kbase, tn), kPlus3, i);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    matrix_half(min(j + 1, T - 1), j);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
+    if (j + 1 < T) {
+      softmax(j + 1, Slot<0>{});
+      vector_tail(((R + 2) % kSlots) * kKTileBytes, kNext, ring);
+    }
+  };
+
+  __syncthreads();
+  if (group == 1) __syncthreads();
+  // QK^T(0) from slot 0, then the vector half-step of tile 0
+#pragma unroll
+  for (int step = 16; step < 32; ++step) matrix_step(step, frag(step, 0, 0));
+  __syncthreads();
+  bf16x8_t ring[kPre];
+  softmax(0, Slot<1>{});
+  vector_tail(1 * kKTileBytes, 0, ring);
+  int j = 0;
+  for (; j + kSlots <= T; j += kSlots) {
+    iteration(j, Slot<0>{}, ring);
+    iteration(j + 1, Slot<1>{}, ring);
+    iteration(j + 2, Slot<2>{}, ring);
+    iteration(j + 3, Slot<3>{}, ring);
   }
+  if (j < T) iteration(j, Slot<0>{}, ring);
+  if (j + 1 < T) iteration(j + 1, Slot<1>{}, ring);
+  if (j + 2 < T) iteration(j + 2, Slot<2>{}, ring);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (group == 0) __syncthreads();
 
   // ---- epilogue: O / l, one bf16 rounding; lane holds query l32 and head
