@@ -120,12 +120,11 @@ fluxattn_status fluxattn_qk_norm_rope_fp8(
  *   q, k, v   bf16 [B,H,N,D] (q and k normally come out of the prologue).
  *   o         bf16 [B,H,N,D] output; must not overlap q, k or v.
  *   softmax_scale  <= 0 selects 1/sqrt(D).
- * Q is multiplied by softmax_scale * log2(e) and rounded to bf16 once, so
- * QK^T yields base-2 logits; scores and the softmax run in fp32; the
- * normaliser sums the fp32 probabilities, which are then rounded to bf16
- * for the P.V product; O is accumulated in fp32, divided by the normaliser
- * and rounded once to bf16.  The N x N score matrix is never stored.
- * Deterministic: the same inputs give bitwise the same output.
+ * Scores and the softmax run in fp32 (exponentials in base 2 with the scale
+ * folded in); the normaliser sums the fp32 probabilities, which are then
+ * rounded to bf16 for the P.V product; O is accumulated in fp32, divided by
+ * the normaliser and rounded once to bf16.  The N x N score matrix is never
+ * stored.  Deterministic: the same inputs give bitwise the same output.
  */
 fluxattn_status fluxattn_forward_bf16(
     const void *q, const void *k, const void *v, void *o,

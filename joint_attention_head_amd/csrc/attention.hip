@@ -39,10 +39,9 @@
 //    next vector half-step and written to LDS in the matrix half-step after
 //    that, two tiles ahead.  Buffer-resource loads return 0 past the end of a
 //    head, so ragged tails need no branches; the softmax masks keys >= N.
-//  * Online softmax in base 2 with no arithmetic besides the exponentials:
-//    Q is pre-multiplied by scale * log2 e, and QK^T starts accumulating at
-//    minus the row's running shift b, so the MFMA delivers c*S - b.  The
-//    row maximum is only scanned when the tile's row sum (an upper bound of
+//  * Online softmax in base 2: one FMA per score gives x = c*S - b (c =
+//    scale * log2 e, b = the row's running shift), then p = 2^x.  The row
+//    maximum is only scanned when the tile's row sum (an upper bound of
 //    every probability in it) exceeds 2^16; b then moves up to the maximum
 //    if that exceeds it by more than 8, with O and l rescaled.  O / l is
 //    unchanged by the shift.  l sums the fp32 probabilities; P is rounded
@@ -336,9 +335,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     }
   }
 
-  // ---- queries, pre-multiplied by c = softmax scale * log2(e) (and the
-  // fp8 scales) and rounded to bf16, so that QK^T yields base-2 logits:
-  // qf[kk] = c * Q[q][16kk + 8hi .. +8), q = this lane's row
+  // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
+  // (fp8: widened to bf16, exact)
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
   {
@@ -346,25 +344,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const uint32_t elem = (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi;
-      float x[8];
       if constexpr (FP8) {
-        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
-          const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
-          x[4 * h + 0] = lo[0];
-          x[4 * h + 1] = lo[1];
-          x[4 * h + 2] = up[0];
-          x[4 * h + 3] = up[1];
-        }
+        qf[kk] = __builtin_bit_cast(bf16x8_t, e4m3x8_to_bf16x8(__builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0)));
       } else {
-        const bf16x8_t v = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+        qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[kk][i] = (__bf16)(x[i] * c);
     }
   }
 
@@ -375,12 +359,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   f32x16_t s[2];
   bf16x8_t pf[4];
-  // QK^T starts its accumulation at -b (b = this row's running shift in
-  // base-2 units), so the scores arrive as c*S - b and the exponentials
-  // need no extra arithmetic
-  float b_run = 0.f;
-  f32x16_t bias = {};
+  float b_run = 0.f;      // this row's running shift, base-2 units
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+  const f32x16_t zero = {};
 
   // Matrix half-step as a 32-step software pipeline over operand fragments:
   // steps 0..15 are PV of the current tile (16-key step st = s/4, head-dim
@@ -401,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   auto matrix_step = [&](int step, bf16x8_t f) __attribute__((always_inline)) {
     if (step >= 16) {
       const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : bias, 0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : zero, 0, 0, 0);
     } else {
       const int st = step >> 2, db = step & 3;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
@@ -409,8 +390,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   };
 
   // Online softmax of tile j.  Lane owns query l32 and keys
-  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]),
-  // as x = c*S - b.  Common case: p = 2^x straight away; the row maximum is
+  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]);
+  // one FMA per score turns S into x = c*S - b (c = softmax scale *
+  // log2 e).  Common case: p = 2^x straight away; the row maximum is
   // only needed when some p may be large, which the tile's own row sum
   // (>= every p in it) tells.  Then, or on the first tile, b moves up to the
   // row maximum when that exceeds it by more than 8 (first tile: moves to
@@ -418,6 +400,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // always and O / l is unchanged.
   auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value != 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
     if (j * kBC + kBC > N) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -466,8 +452,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       if (kFirst || __builtin_amdgcn_ballot_w64(mx > 8.0f) != 0) {
         const float d = kFirst ? mx : fmaxf(mx, 0.f);
         b_run += d;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bias[i] = -b_run;
         if constexpr (!kFirst) {
           const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll

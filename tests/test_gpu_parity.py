@@ -193,6 +193,31 @@ def test_forward_bf16_custom_scale():
     check_close(f64(o), ref, BF16_TOL, "forward bf16 scale=0.05")
 
 
+@pytest.mark.parametrize("growth", ["rising", "falling", "spike"])
+def test_forward_bf16_logit_range_across_tiles(growth):
+    """Scores whose scale changes from one 64-key tile to the next, so the
+    running shift of the online softmax has to move by far more than the
+    lazy threshold (rising: later tiles dominate by tens of log2 units;
+    falling: the first tile dominates and later ones underflow towards 0;
+    spike: one key tile far above everything before it)."""
+    inp = small(1, 2, 37, (20, 20))          # N = 437: 7 key tiles, ragged
+    N = inp.q.shape[2]
+    f = torch.ones(N)
+    tiles = torch.arange(N) // 64
+    if growth == "rising":
+        f = 1.0 + tiles.float()               # logit spread grows 7x
+    elif growth == "falling":
+        f = torch.where(tiles == 0, 6.0, 1.0)
+    else:
+        f = torch.where(tiles == 4, 9.0, 1.0)
+    k = (inp.k.float() * f[None, None, :, None]).to(torch.bfloat16)
+    o = fa.fluxattn_forward_bf16(dev(inp.q), dev(k), dev(inp.v))
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(inp.q), f64(k), f64(inp.v))
+    rel = check_close(f64(o), ref, BF16_TOL, f"logit range {growth}")
+    assert rel < 1e-2
+
+
 def test_forward_bf16_invariants():
     inp = small(1, 2, 13, (10, 10))
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
