@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Joint-attention throughput on one MI355X.
 
-One step = the whole hot path over one batch: the fused QK-RMSNorm + 3-axis
-RoPE prologue, then non-causal softmax attention, on the 2048x2048
+One step = the whole hot path over one batch: per-head RMSNorm + 3-axis RoPE
+of queries and keys, then non-causal softmax attention, on the 2048x2048
 text-to-image workload with CFG (B=2, H=24, N = 512 text + 128x128 image
-tokens = 16896, d=128, bf16), inputs already resident in HBM.
+tokens = 16896, d=128, bf16), inputs already resident in HBM.  Default path
+(--path fused): the keys-only prologue kernel, then the attention kernel
+that normalises and rotates the queries as it loads them; --path unfused
+runs the prologue on both and the plain attention kernel.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 
@@ -41,9 +44,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path: str):
     """HBM bytes per forward launch from the committed rocprofv3 counter
-    summary, or None if the kernel source changed since it was taken."""
+    summary, or None if the kernel source changed since it was taken or the
+    summary covers the other kernel variant."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -52,7 +56,7 @@ def measured_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash() or vals.get("path", "unfused") != path:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -69,12 +73,13 @@ def parse():
     p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
+    p.add_argument("--path", choices=("fused", "unfused"), default="fused")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
 
 
-def run_gpu(name: str, steps: int, warmup: int):
+def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
     import torch
 
     import joint_attention_head_amd as fa
@@ -91,10 +96,16 @@ def run_gpu(name: str, steps: int, warmup: int):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos, q_out=qn, k_out=kn, stream=stream)
+        if path == "fused":
+            fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos, k_out=kn, stream=stream)
+        else:
+            fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos, q_out=qn, k_out=kn, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
+        if path == "fused":
+            fa.fluxattn_forward_fused_bf16(q, kn, v, w_q, pos, o=o, stream=stream)
+        else:
+            fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -113,7 +124,8 @@ def run_gpu(name: str, steps: int, warmup: int):
     span = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3
     assert torch.isfinite(o).all().item()
     flops = w.flops
-    prologue_bytes = 4.0 * w.B * w.H * w.N * 128 * 2      # read + write Q and K
+    # read + write K (fused path) or Q and K
+    prologue_bytes = (2.0 if path == "fused" else 4.0) * w.B * w.H * w.N * 128 * 2
     attn_min_bytes = 4.0 * w.B * w.H * w.N * 128 * 2      # read Q, K, V, write O once
     t_fwd = sum(fwd) / len(fwd)
     t_pro = sum(pro) / len(pro)
@@ -189,11 +201,11 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
-    main_res = run_gpu(args.workload, args.steps, args.warmup)
+    main_res = run_gpu(args.workload, args.steps, args.warmup, args.path)
     print(f"bench: {args.workload} forward {main_res['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
     also = None
     if args.also:
-        r = run_gpu(args.also, args.steps, args.warmup)
+        r = run_gpu(args.also, args.steps, args.warmup, args.path)
         w = r["workload"]
         also = {
             "workload": f"{w.name}: B={w.B} H={w.H} N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128 bf16",
@@ -212,7 +224,7 @@ def main():
         cpu = cpu_baseline(args.workload, args.cpu_heads)
 
     w = main_res["workload"]
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.path)
     line = {
         "metric": "joint-attention TFLOP/s and % MFMA peak at N=4608 and N=16896, 1 GPU",
         "value": round(main_res["value"], 2),
@@ -229,10 +241,11 @@ def main():
         "config": {
             "workload": f"{w.name}: 2048x2048 text-to-image with CFG, B={w.B} H={w.H} "
                         f"N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128, prologue + attention",
+            "path": args.path,
             "B": w.B, "H": w.H, "N": w.N, "head_dim": 128,
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel (bf16)",
+            "kernel": "attn_fwd_kernel (bf16, %s)" % ("fused query prologue" if args.path == "fused" else "plain"),
             "bound": "mfma",
             "achieved": round(main_res["forward_tflops"], 2),
             "peak": BF16_PEAK_TFLOPS,
@@ -242,7 +255,7 @@ def main():
             "launch_ms": round(main_res["forward_ms"], 4),
         },
         "prologue": {
-            "kernel": "prologue_bf16_kernel",
+            "kernel": "prologue_bf16_kernel (%s)" % ("keys only" if args.path == "fused" else "queries and keys"),
             "bound": "hbm",
             "achieved": round(main_res["prologue_gbs"], 1),
             "peak": HBM_PEAK_GBS,

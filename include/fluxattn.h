@@ -80,6 +80,9 @@ typedef enum {
  *   pos_ids       int32 [N,3] (t,h,w) token positions.
  *   axes_*, theta RoPE axis split and base (FLUX: 16, 56, 56 and 1e4).
  *   eps           RMSNorm epsilon (FLUX: 1e-6), inside the square root.
+ * Keys only: q, q_out and q_norm_w all NULL processes k alone (the form
+ * the fused attention entry points below pair with); a NULL among them
+ * otherwise is FLUXATTN_ERR_NULL_POINTER.
  * Rotation angles are evaluated in fp32 from the integer ids and fp32
  * frequencies (rounded from fp64 on the host); sums of squares are fp32.
  */
@@ -102,7 +105,8 @@ fluxattn_status fluxattn_qk_norm_rope_bf16(
  *                 sqrt(D) * max|w| / 448 for the matching weight vector.
  *                 Every prologue output is bounded by sqrt(D) * max|w| in
  *                 magnitude, so the encode never saturates.
- * Other arguments as in fluxattn_qk_norm_rope_bf16.
+ * Other arguments as in fluxattn_qk_norm_rope_bf16; keys only when q,
+ * q_scale, q_out, q_scale_out and q_norm_w are all NULL.
  */
 fluxattn_status fluxattn_qk_norm_rope_fp8(
     const uint8_t *q, const uint8_t *k, const float *q_scale,
@@ -142,6 +146,81 @@ fluxattn_status fluxattn_forward_fp8(
     const float *q_scale, const float *k_scale, const float *v_scale,
     void *o, int64_t B, int64_t H, int64_t N, int64_t D, float softmax_scale,
     void *stream);
+
+/*
+ * Attention on raw (pre-norm) queries: the kernel's query load applies the
+ * queries' RMSNorm + RoPE in registers, so Q' never goes to memory; k must
+ * already hold K' (e.g. from the keys-only prologue above).  (blog post
+ * above, section "GEMM kernel optimization": the pages fuse this step into
+ * the QKV projection's epilogue; here it is fused into its consumer.)
+ *   q         bf16 [B,H,N,D] raw queries.
+ *   k, v      bf16 [B,H,N,D] prepared keys, values.
+ *   o         bf16 [B,H,N,D] output; must not overlap any input.
+ *   q_norm_w  fp32 [D] query RMSNorm weights, 16-byte aligned.
+ *   pos_ids, axes_*, theta, eps  as in fluxattn_qk_norm_rope_bf16.
+ *   softmax_scale  as in fluxattn_forward_bf16.
+ * Q' is computed in fp32 and rounded to bf16 once, as the prologue would
+ * store it.  The rotation frequencies are 2^(j * -2 log2(theta) / axes_a)
+ * evaluated on the device (within 1e-6 relative of the host table the
+ * prologue uses) and the angles go through the hardware sine / cosine
+ * after reduction to one revolution (absolute error about
+ * 1e-6 + 4e-8 |angle| rad).  Numerics otherwise as fluxattn_forward_bf16.
+ */
+fluxattn_status fluxattn_forward_fused_bf16(
+    const void *q, const void *k, const void *v, void *o,
+    const float *q_norm_w, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
+
+/*
+ * fp8 form: E4M3 q (raw), k (prepared), v with fp32 [B,H] scales; the
+ * queries are dequantised, normalised and rotated in fp32 and kept in
+ * bf16.  Output bf16.
+ */
+fluxattn_status fluxattn_forward_fused_fp8(
+    const uint8_t *q, const uint8_t *k, const uint8_t *v,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    void *o, const float *q_norm_w, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
+
+/*
+ * The whole block in two launches: the keys-only prologue into k_work,
+ * then fluxattn_forward_fused_bf16 on the raw queries.
+ *   q, k, v    bf16 [B,H,N,D]: raw (pre-norm) queries and keys, values.
+ *   k_work     bf16 [B,H,N,D], receives K'; may equal k (in place), must
+ *              not overlap any other buffer.
+ *   o          bf16 [B,H,N,D] output; must not overlap any other buffer.
+ *   q_norm_w   fp32 [D], 16-byte aligned; k_norm_w fp32 [D].
+ *   Other arguments as in fluxattn_qk_norm_rope_bf16 and
+ *   fluxattn_forward_bf16.  Results match those two calls up to fp32
+ *   summation order and the query rotation, computed as in
+ *   fluxattn_forward_fused_bf16.
+ */
+fluxattn_status fluxattn_joint_attention_bf16(
+    const void *q, const void *k, const void *v, void *k_work, void *o,
+    const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
+
+/*
+ * fp8 form of fluxattn_joint_attention_bf16: E4M3 q, k, v with fp32 [B,H]
+ * scales.  The fp8 key prologue writes k_work (E4M3) and k_scale_work
+ * (fp32 [B,H], must not overlap k_scale); the queries are dequantised,
+ * normalised and rotated in the attention kernel and kept in bf16, which is
+ * more precise than the E4M3 Q' of the two-call path.  Output bf16.
+ */
+fluxattn_status fluxattn_joint_attention_fp8(
+    const uint8_t *q, const uint8_t *k, const uint8_t *v,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    uint8_t *k_work, float *k_scale_work, void *o,
+    const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *fluxattn_status_string(fluxattn_status s);

@@ -12,6 +12,10 @@ Entry points (same names as the C ABI):
     fluxattn_qk_norm_rope_fp8(q, k, q_scale, k_scale, q_norm_w, k_norm_w, pos_ids, ...)
     fluxattn_forward_bf16(q, k, v, ...)
     fluxattn_forward_fp8(q, k, v, q_scale, k_scale, v_scale, ...)
+    fluxattn_forward_fused_bf16(q, k, v, q_norm_w, pos_ids, ...)
+    fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos_ids, ...)
+    fluxattn_joint_attention_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, ...)
+    fluxattn_joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids, ...)
 """
 from __future__ import annotations
 
@@ -42,6 +46,10 @@ EXPORTS = (
     "fluxattn_qk_norm_rope_fp8",
     "fluxattn_forward_bf16",
     "fluxattn_forward_fp8",
+    "fluxattn_forward_fused_bf16",
+    "fluxattn_forward_fused_fp8",
+    "fluxattn_joint_attention_bf16",
+    "fluxattn_joint_attention_fp8",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
     "fluxattn_version",
@@ -69,6 +77,14 @@ _SIGS = {
                                   _i32, _i32, _i32, _f, _f, _p],
     "fluxattn_forward_bf16": [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p],
     "fluxattn_forward_fp8": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f, _p],
+    "fluxattn_forward_fused_bf16": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                    _f, _f, _f, _p],
+    "fluxattn_forward_fused_fp8": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32,
+                                   _i32, _f, _f, _f, _p],
+    "fluxattn_joint_attention_bf16": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64,
+                                      _i32, _i32, _i32, _f, _f, _f, _p],
+    "fluxattn_joint_attention_fp8": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
+                                     _i64, _i32, _i32, _i32, _f, _f, _f, _p],
 }
 
 
@@ -128,54 +144,64 @@ def _bhnd(q: torch.Tensor):
     return tuple(q.shape)
 
 
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
 def fluxattn_qk_norm_rope_bf16(q, k, q_norm_w, k_norm_w, pos_ids, q_out=None, k_out=None,
                                axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, stream=None):
     """RMSNorm + 3-axis RoPE of bf16 q, k [B,H,N,D]; returns (q_out, k_out).
-    Pass q_out=q / k_out=k to work in place."""
-    B, H, N, D = _bhnd(q)
-    _need(q, "q", torch.bfloat16)
-    _need(k, "k", torch.bfloat16, q.shape)
-    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    Pass q_out=q / k_out=k to work in place; q=None (with q_norm_w=None)
+    processes the keys only and returns (None, k_out)."""
+    B, H, N, D = _bhnd(k)
+    _need(k, "k", torch.bfloat16)
+    if q is not None:
+        _need(q, "q", torch.bfloat16, k.shape)
+        _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        _need(q_out, "q_out", torch.bfloat16, k.shape)
     _need(k_norm_w, "k_norm_w", torch.float32, (D,))
     _need(pos_ids, "pos_ids", torch.int32, (N, 3))
-    q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
-    _need(q_out, "q_out", torch.bfloat16, q.shape)
-    _need(k_out, "k_out", torch.bfloat16, q.shape)
+    _need(k_out, "k_out", torch.bfloat16, k.shape)
     _check(lib().fluxattn_qk_norm_rope_bf16(
-        q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), q_norm_w.data_ptr(),
-        k_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2],
-        float(theta), float(eps), _stream(stream)))
-    return q_out, k_out
+        _ptr(q), k.data_ptr(), _ptr(q_out) if q is not None else None, k_out.data_ptr(),
+        _ptr(q_norm_w) if q is not None else None, k_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D,
+        axes[0], axes[1], axes[2], float(theta), float(eps), _stream(stream)))
+    return (q_out if q is not None else None), k_out
 
 
 def fluxattn_qk_norm_rope_fp8(q, k, q_scale, k_scale, q_norm_w, k_norm_w, pos_ids, q_out=None,
                               k_out=None, q_scale_out=None, k_scale_out=None, axes=ROPE_AXES,
                               theta=ROPE_THETA, eps=RMS_EPS, stream=None):
     """The prologue on float8_e4m3fn q, k with fp32 [B,H] scales; returns
-    (q_out, k_out, q_scale_out, k_scale_out)."""
-    B, H, N, D = _bhnd(q)
+    (q_out, k_out, q_scale_out, k_scale_out).  q=None (with q_scale and
+    q_norm_w None) processes the keys only; the q entries are then None."""
+    B, H, N, D = _bhnd(k)
     e4 = torch.float8_e4m3fn
-    _need(q, "q", e4)
-    _need(k, "k", e4, q.shape)
-    _need(q_scale, "q_scale", torch.float32, (B, H))
+    _need(k, "k", e4)
     _need(k_scale, "k_scale", torch.float32, (B, H))
-    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    if q is not None:
+        _need(q, "q", e4, k.shape)
+        _need(q_scale, "q_scale", torch.float32, (B, H))
+        _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        q_scale_out = torch.empty_like(q_scale) if q_scale_out is None else q_scale_out
+        _need(q_out, "q_out", e4, k.shape)
+        _need(q_scale_out, "q_scale_out", torch.float32, (B, H))
+    else:
+        q_scale, q_out, q_scale_out, q_norm_w = None, None, None, None
     _need(k_norm_w, "k_norm_w", torch.float32, (D,))
     _need(pos_ids, "pos_ids", torch.int32, (N, 3))
-    q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
-    q_scale_out = torch.empty_like(q_scale) if q_scale_out is None else q_scale_out
     k_scale_out = torch.empty_like(k_scale) if k_scale_out is None else k_scale_out
-    _need(q_out, "q_out", e4, q.shape)
-    _need(k_out, "k_out", e4, q.shape)
-    _need(q_scale_out, "q_scale_out", torch.float32, (B, H))
+    _need(k_out, "k_out", e4, k.shape)
     _need(k_scale_out, "k_scale_out", torch.float32, (B, H))
     _check(lib().fluxattn_qk_norm_rope_fp8(
-        q.data_ptr(), k.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), q_out.data_ptr(),
-        k_out.data_ptr(), q_scale_out.data_ptr(), k_scale_out.data_ptr(), q_norm_w.data_ptr(),
-        k_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2],
-        float(theta), float(eps), _stream(stream)))
+        _ptr(q), k.data_ptr(), _ptr(q_scale), k_scale.data_ptr(), _ptr(q_out), k_out.data_ptr(),
+        _ptr(q_scale_out), k_scale_out.data_ptr(), _ptr(q_norm_w), k_norm_w.data_ptr(),
+        pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps),
+        _stream(stream)))
     return q_out, k_out, q_scale_out, k_scale_out
 
 
@@ -221,3 +247,97 @@ def joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, 
     qn, kn, sq, sk = fluxattn_qk_norm_rope_fp8(q, k, q_scale, k_scale, q_norm_w, k_norm_w, pos_ids,
                                                axes=axes, theta=theta, eps=eps, stream=stream)
     return fluxattn_forward_fp8(qn, kn, v, sq, sk, v_scale, stream=stream)
+
+
+def fluxattn_joint_attention_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, o=None, k_work=None,
+                                  axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0,
+                                  stream=None):
+    """The whole block on raw bf16 q, k, v [B,H,N,D] in two launches: the
+    keys' RMSNorm + RoPE into k_work (pass k_work=k to overwrite k), then
+    attention that normalises and rotates the queries as it loads them.
+    Returns o."""
+    B, H, N, D = _bhnd(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, q.shape)
+    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    _need(k_norm_w, "k_norm_w", torch.float32, (D,))
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty_like(q) if o is None else o
+    k_work = torch.empty_like(k) if k_work is None else k_work
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(k_work, "k_work", torch.bfloat16, q.shape)
+    _check(lib().fluxattn_joint_attention_bf16(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), k_work.data_ptr(), o.data_ptr(), q_norm_w.data_ptr(),
+        k_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta),
+        float(eps), float(softmax_scale), _stream(stream)))
+    return o
+
+
+def fluxattn_joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids,
+                                 o=None, k_work=None, k_scale_work=None, axes=ROPE_AXES,
+                                 theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, stream=None):
+    """The whole block on raw float8_e4m3fn q, k, v with fp32 [B,H] scales:
+    the fp8 key prologue into (k_work, k_scale_work), then attention that
+    normalises and rotates the queries as it loads them (kept in bf16).
+    Returns bf16 o."""
+    B, H, N, D = _bhnd(q)
+    e4 = torch.float8_e4m3fn
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, e4, q.shape)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, (B, H))
+    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    _need(k_norm_w, "k_norm_w", torch.float32, (D,))
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    k_work = torch.empty_like(k) if k_work is None else k_work
+    k_scale_work = torch.empty_like(k_scale) if k_scale_work is None else k_scale_work
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(k_work, "k_work", e4, q.shape)
+    _need(k_scale_work, "k_scale_work", torch.float32, (B, H))
+    _check(lib().fluxattn_joint_attention_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), k_work.data_ptr(), k_scale_work.data_ptr(), o.data_ptr(),
+        q_norm_w.data_ptr(), k_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1],
+        axes[2], float(theta), float(eps), float(softmax_scale), _stream(stream)))
+    return o
+
+
+def fluxattn_forward_fused_bf16(q, k, v, q_norm_w, pos_ids, o=None, axes=ROPE_AXES, theta=ROPE_THETA,
+                                eps=RMS_EPS, softmax_scale=0.0, stream=None):
+    """Attention on raw bf16 queries (RMSNorm + RoPE applied as they are
+    loaded) against prepared keys k and values v; returns o."""
+    B, H, N, D = _bhnd(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, q.shape)
+    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty_like(q) if o is None else o
+    _need(o, "o", torch.bfloat16, q.shape)
+    _check(lib().fluxattn_forward_fused_bf16(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), q_norm_w.data_ptr(), pos_ids.data_ptr(),
+        B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps), float(softmax_scale),
+        _stream(stream)))
+    return o
+
+
+def fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos_ids, o=None,
+                               axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0,
+                               stream=None):
+    """fp8 form of fluxattn_forward_fused_bf16 (E4M3 q raw, k prepared, v;
+    fp32 [B,H] scales); returns bf16 o."""
+    B, H, N, D = _bhnd(q)
+    e4 = torch.float8_e4m3fn
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, e4, q.shape)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, (B, H))
+    _need(q_norm_w, "q_norm_w", torch.float32, (D,))
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    _need(o, "o", torch.bfloat16, q.shape)
+    _check(lib().fluxattn_forward_fused_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), o.data_ptr(), q_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0],
+        axes[1], axes[2], float(theta), float(eps), float(softmax_scale), _stream(stream)))
+    return o

@@ -143,7 +143,87 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
+// Queries of the fused entry points: raw Q (fp8: times its scale) ->
+// RMSNorm over the 128 dims -> rotation of each adjacent pair by its
+// axis position times frequency -> bf16 (the prologue's operations, on the
+// 64 dims this lane holds: 16 kk + 8 hi + i; the other 64 are in lane ^ 32).
 template <bool FP8>
+__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const char *qbase,
+                                             uint32_t head_bytes, int q_row, int hi, float q_scale) {
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
+  // raw codes / values stay packed until the transform
+  u32x2_t raw8[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const uint32_t elem = (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi;
+    if constexpr (FP8) {
+      raw8[kk] = __builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0);
+    } else {
+      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
+    }
+  }
+  auto values = [&](int kk, float (&x)[8]) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw8[kk][h], false);
+        const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw8[kk][h], true);
+        x[4 * h + 0] = lo[0] * q_scale;
+        x[4 * h + 1] = lo[1] * q_scale;
+        x[4 * h + 2] = up[0] * q_scale;
+        x[4 * h + 3] = up[1] * q_scale;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)qf[kk][i];
+    }
+  };
+  float ss = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    float x[8];
+    values(kk, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
+    ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
+  }
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  // position ids of this query (rows past N belong to no token: any valid
+  // row serves, their outputs are never stored)
+  const int tok = min(q_row, a.N - 1);
+  const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    float x[8];
+    values(kk, x);
+    const float4 w0 = *reinterpret_cast<const float4 *>(a.w_q + 16 * kk + 8 * hi);
+    const float4 w1 = *reinterpret_cast<const float4 *>(a.w_q + 16 * kk + 8 * hi + 4);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // pair pr = 8 kk + 4 hi + m: its axis, index inside the axis, angle
+      const int pr = 8 * kk + 4 * hi + m;
+      const int ax = pr < a.rope_first[1] ? 0 : (pr < a.rope_first[2] ? 1 : 2);
+      const int jj = pr - (ax == 0 ? 0 : (ax == 1 ? a.rope_first[1] : a.rope_first[2]));
+      const float step = ax == 0 ? a.rope_log2_step[0] : (ax == 1 ? a.rope_log2_step[1] : a.rope_log2_step[2]);
+      const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
+      // angle in revolutions, reduced to [0, 1) and fed to the hardware
+      // sin / cos: absolute error about 1e-6 + 4e-8 |angle| rad, the size
+      // of the fp32 rounding of the angle itself for FLUX's positions
+      const float rev = __builtin_amdgcn_fractf((float)p * exp2f((float)jj * step) * 0.15915494309189535f);
+      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      const float u = x[2 * m] * w[2 * m] * rstd;
+      const float v = x[2 * m + 1] * w[2 * m + 1] * rstd;
+      qf[kk][2 * m] = (__bf16)(u * cs - v * sn);
+      qf[kk][2 * m + 1] = (__bf16)(u * sn + v * cs);
+    }
+  }
+}
+
+template <bool FP8, bool FUSEQ>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int simd_of_wave[kWaves];
@@ -188,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   float c = a.scale_log2;
   float o_scale = 1.f;
   if constexpr (FP8) {
-    c *= a.q_scale[bh] * a.k_scale[bh];
+    c *= (FUSEQ ? 1.f : a.q_scale[bh]) * a.k_scale[bh];   // fused: Q arrives in true units
     o_scale = a.v_scale[bh];
   }
   const int T = (N + kBC - 1) / kBC;
@@ -339,7 +419,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // (fp8: widened to bf16, exact)
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
-  {
+  if constexpr (FUSEQ) {
+    load_q_fused<FP8>(qf, a, qbase, head_bytes, q_row, hi, FP8 ? a.q_scale[bh] : 1.f);
+  } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -600,7 +682,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     }
 }
 
-template <bool FP8>
+template <bool FP8, bool FUSEQ>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.N + kBR - 1) / kBR;
   const int64_t grid = ntiles * a.BH;
@@ -612,19 +694,21 @@ hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FP8>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FP8, FUSEQ>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<FP8, FUSEQ>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s) { return launch<false>(a, s); }
-hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s) { return launch<true>(a, s); }
+hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s) { return launch<false, false>(a, s); }
+hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s) { return launch<true, false>(a, s); }
+hipError_t launch_forward_fused_bf16(const ForwardArgs &a, hipStream_t s) { return launch<false, true>(a, s); }
+hipError_t launch_forward_fused_fp8(const ForwardArgs &a, hipStream_t s) { return launch<true, true>(a, s); }
 
 int64_t forward_grid_blocks(int64_t BH, int64_t N) { return BH * ((N + kBR - 1) / kBR); }
 

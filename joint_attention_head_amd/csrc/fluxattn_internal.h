@@ -35,6 +35,15 @@ struct ForwardArgs {
   int32_t BH;
   int32_t N;
   float scale_log2;   // softmax_scale * log2(e)
+  // fused query prologue only: raw q is normalised and rotated on load.
+  // Pair p of axis a (pairs rope_first[a] .. rope_first[a+1]-1) turns by
+  // pos[a] * 2^((p - rope_first[a]) * rope_log2_step[a]), with
+  // rope_log2_step[a] = -2 log2(theta) / axes[a].
+  const float *w_q;
+  const int32_t *pos;
+  float eps;
+  int32_t rope_first[4];
+  float rope_log2_step[3];
 };
 
 hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
@@ -43,6 +52,9 @@ hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
                                hipStream_t s);
 hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s);
 hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s);
+// attention whose Q load applies RMSNorm + RoPE to raw queries
+hipError_t launch_forward_fused_bf16(const ForwardArgs &a, hipStream_t s);
+hipError_t launch_forward_fused_fp8(const ForwardArgs &a, hipStream_t s);
 
 // Workgroups the forward kernel launches for B*H heads of N tokens.
 int64_t forward_grid_blocks(int64_t BH, int64_t N);

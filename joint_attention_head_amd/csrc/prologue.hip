@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
   float cs[4], sn[4];
   lane_angles(a, t, tok, c, cs, sn);
 
-  for (int which = 0; which < 2; ++which) {
+  for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint16_t *src = static_cast<const uint16_t *>(which ? a.k : a.q);
     uint16_t *dst = static_cast<uint16_t *>(which ? a.k_out : a.q_out);
     const float *wp = which ? a.w_k : a.w_q;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
   // Output scale sqrt(D) * max|w| / 448: every output lies within +-448 of it.
   float sq, sk;
   {
-    const float mq = wave_max(fmaxf(fabsf(a.w_q[lane]), fabsf(a.w_q[lane + 64])));
+    const float mq = a.w_q ? wave_max(fmaxf(fabsf(a.w_q[lane]), fabsf(a.w_q[lane + 64]))) : 0.f;
     const float mk = wave_max(fmaxf(fabsf(a.w_k[lane]), fabsf(a.w_k[lane + 64])));
     const float root_d = 11.313708498984760f;  // sqrt(128)
     sq = mq > 0.f ? root_d * mq / 448.f : 1.f;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
   }
   if (blockIdx.x == 0) {
     for (int64_t i = threadIdx.x; i < a.BH; i += kThreads) {
-      a.q_scale_out[i] = sq;
+      if (a.q_scale_out) a.q_scale_out[i] = sq;
       a.k_scale_out[i] = sk;
     }
   }
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
   float cs[4], sn[4];
   lane_angles(a, t, tok, c, cs, sn);
 
-  for (int which = 0; which < 2; ++which) {
+  for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint8_t *src = static_cast<const uint8_t *>(which ? a.k : a.q);
     uint8_t *dst = static_cast<uint8_t *>(which ? a.k_out : a.q_out);
     const float *wp = which ? a.w_k : a.w_q;

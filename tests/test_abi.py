@@ -70,6 +70,31 @@ def forward8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, o=O, b=B, h=H, n=N, d=D):
     return lib.fluxattn_forward_fp8(q, k, v, sq, sk, sv, o, b, h, n, d, 0.0, None)
 
 
+KW = 0x70000000
+SKW = 0xA0008000
+
+
+def joint(lib, q=Q, k=K, v=V, kw=KW, o=O, wq=WQ, wk=WK, pos=POS, b=B, h=H, n=N, d=D,
+          axes=(16, 56, 56), theta=1e4, eps=1e-6, scale=0.0):
+    return lib.fluxattn_joint_attention_bf16(q, k, v, kw, o, wq, wk, pos, b, h, n, d, *axes, theta, eps,
+                                             scale, None)
+
+
+def joint8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, kw=KW, skw=SKW, o=O, wq=WQ, wk=WK, pos=POS,
+           b=B, h=H, n=N, d=D):
+    return lib.fluxattn_joint_attention_fp8(q, k, v, sq, sk, sv, kw, skw, o, wq, wk, pos, b, h, n, d,
+                                            16, 56, 56, 1e4, 1e-6, 0.0, None)
+
+
+def fused(lib, q=Q, k=K, v=V, o=O, wq=WQ, pos=POS, b=B, h=H, n=N, d=D, scale=0.0):
+    return lib.fluxattn_forward_fused_bf16(q, k, v, o, wq, pos, b, h, n, d, 16, 56, 56, 1e4, 1e-6, scale, None)
+
+
+def fused8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, o=O, wq=WQ, pos=POS, b=B, h=H, n=N, d=D):
+    return lib.fluxattn_forward_fused_fp8(q, k, v, sq, sk, sv, o, wq, pos, b, h, n, d, 16, 56, 56, 1e4, 1e-6,
+                                          0.0, None)
+
+
 def test_null_pointers(lib):
     for kw in ("q", "k", "qo", "ko", "wq", "wk", "pos"):
         assert prologue(lib, **{kw: None}) == NULLP, kw
@@ -79,6 +104,21 @@ def test_null_pointers(lib):
         assert forward(lib, **{kw: None}) == NULLP, kw
     for kw in ("q", "k", "v", "sq", "sk", "sv", "o"):
         assert forward8(lib, **{kw: None}) == NULLP, kw
+    for kw in ("q", "k", "v", "kw", "o", "wq", "wk", "pos"):
+        assert joint(lib, **{kw: None}) == NULLP, kw
+    for kw in ("q", "k", "v", "o", "wq", "pos"):
+        assert fused(lib, **{kw: None}) == NULLP, kw
+    for kw in ("q", "k", "v", "sq", "sk", "sv", "o", "wq", "pos"):
+        assert fused8(lib, **{kw: None}) == NULLP, kw
+    # keys-only prologue: q, q_out, q_norm_w all NULL; any one of them alone is an error
+    assert prologue(lib, q=None, qo=None, wq=None) != NULLP
+    assert prologue(lib, q=None, qo=None) == NULLP
+    assert prologue(lib, q=None, wq=None) == NULLP
+    assert prologue8(lib, q=None, qo=None, sq=None, sqo=None) == NULLP       # q_norm_w still set
+    assert lib.fluxattn_qk_norm_rope_fp8(None, K, None, SK, None, KO, None, SKO, None, WK, POS, B, H, N, D,
+                                         16, 56, 56, 1e4, 1e-6, None) != NULLP
+    for kw in ("q", "k", "v", "sq", "sk", "sv", "kw", "skw", "o", "wq", "wk", "pos"):
+        assert joint8(lib, **{kw: None}) == NULLP, kw
 
 
 def test_invalid_shapes(lib):
@@ -87,6 +127,13 @@ def test_invalid_shapes(lib):
         assert forward(lib, **kw) == SHAPE, kw
         assert prologue8(lib, **kw) == SHAPE, kw
         assert forward8(lib, **kw) == SHAPE, kw
+        assert joint(lib, **kw) == SHAPE, kw
+        assert fused(lib, **kw) == SHAPE, kw
+        assert fused8(lib, **kw) == SHAPE, kw
+        assert joint8(lib, **kw) == SHAPE, kw
+    assert joint(lib, axes=(16, 56, 54)) == SHAPE
+    assert joint(lib, theta=-1.0) == SHAPE
+    assert joint(lib, scale=float("nan")) == SHAPE
     assert prologue(lib, axes=(16, 56, 54)) == SHAPE     # does not sum to D
     assert prologue(lib, axes=(15, 57, 56)) == SHAPE     # odd axis
     assert prologue(lib, axes=(-16, 88, 56)) == SHAPE
@@ -107,6 +154,11 @@ def test_misaligned(lib):
     assert forward(lib, v=V + 8) == ALIGN
     assert forward8(lib, sv=SV + 2) == ALIGN
     assert prologue8(lib, sqo=SQO + 1) == ALIGN
+    assert joint(lib, wq=WQ + 4) == ALIGN        # the fused query load reads 16-byte weight vectors
+    assert fused(lib, wq=WQ + 4) == ALIGN
+    assert fused8(lib, sq=SQ + 2) == ALIGN
+    assert joint(lib, kw=KW + 8) == ALIGN
+    assert joint8(lib, skw=SKW + 2) == ALIGN
 
 
 def test_aliasing(lib):
@@ -122,6 +174,16 @@ def test_aliasing(lib):
     assert prologue(lib, ko=POS - 16) == ALIAS
     assert prologue8(lib, sqo=SQ) == ALIAS
     assert prologue8(lib, sko=SQO) == ALIAS
+    # fused path: k_work may be k itself, nothing else may overlap
+    assert joint(lib, kw=K + 16) == ALIAS
+    assert joint(lib, kw=V) == ALIAS
+    assert joint(lib, o=KW) == ALIAS
+    assert joint(lib, o=Q + 32) == ALIAS
+    assert joint8(lib, skw=SK) == ALIAS          # scales read while the new ones are written
+    assert joint8(lib, skw=SQ) == ALIAS
+    assert fused(lib, o=K) == ALIAS
+    assert fused(lib, o=WQ - 64) == ALIAS
+    assert fused8(lib, o=SV) == ALIAS
 
 
 def test_valid_calls_need_a_gfx950_device(lib):
@@ -137,6 +199,14 @@ def test_valid_calls_need_a_gfx950_device(lib):
     assert prologue8(lib) == NODEV
     assert forward(lib) == NODEV
     assert forward8(lib) == NODEV
+    assert joint(lib) == NODEV
+    assert joint(lib, kw=K) == NODEV             # in place passes aliasing
+    assert joint8(lib) == NODEV
+    assert fused(lib) == NODEV
+    assert fused8(lib) == NODEV
+    assert prologue(lib, q=None, qo=None, wq=None) == NODEV
+    assert lib.fluxattn_qk_norm_rope_fp8(None, K, None, SK, None, KO, None, SKO, None, WK, POS, B, H, N, D,
+                                         16, 56, 56, 1e4, 1e-6, None) == NODEV
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -300,6 +300,103 @@ def test_joint_bf16_parity_t2i_2048_sampled():
     assert torch.all(ones == 1.0)
 
 
+FUSED_CASES = {
+    "tiny": lambda: inputs("tiny"),
+    "flux_dev_512": lambda: inputs("flux_dev_512"),
+    "odd_77+256": lambda: small(1, 3, 77, (16, 16)),
+    "ref_t1": lambda: small(2, 2, 9, (10, 12), (6, 7)),
+    "n65": lambda: small(2, 1, 1, (8, 8)),
+}
+
+
+@pytest.mark.parametrize("case", list(FUSED_CASES))
+def test_joint_fused_bf16_parity(case):
+    """Queries' RMSNorm + RoPE inside the attention kernel, keys' prologue
+    into a separate buffer; against the whole fp64 chain."""
+    _flush(f"joint fused bf16 {case}")
+    inp = FUSED_CASES[case]()
+    q, k = dev(inp.q), dev(inp.k)
+    k_keep = k.clone()
+    o = fa.fluxattn_joint_attention_bf16(q, k, dev(inp.v), dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    assert torch.equal(k.view(torch.int16), k_keep.view(torch.int16))   # k untouched
+    rel = check_close(f64(o), joint_ref(inp), BF16_TOL, f"joint fused bf16 {case}")
+    assert rel < 1e-2
+
+
+def test_joint_fused_bf16_in_place_and_matches_two_calls():
+    inp = small(1, 2, 21, (12, 12))
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    two = fa.joint_attention_bf16(q, k, v, w_q, w_k, pos)
+    sep = fa.fluxattn_joint_attention_bf16(q, k, v, w_q, w_k, pos)
+    k2 = k.clone()
+    inplace = fa.fluxattn_joint_attention_bf16(q, k2, v, w_q, w_k, pos, k_work=k2)
+    kn = fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(sep.view(torch.int16), inplace.view(torch.int16))
+    assert torch.equal(k2.view(torch.int16), kn.view(torch.int16))      # k_work holds K'
+    # same block up to where Q' is rounded: differences of a bf16 step at most
+    check_close(f64(sep), f64(two), BF16_TOL, "fused vs two calls")
+
+
+def test_keys_only_prologue_and_fused_forward_compose_the_joint_call():
+    """keys-only prologue == the keys of the full prologue (bitwise), and
+    keys-only prologue + fused forward == the joint entry point (bitwise)."""
+    inp = small(1, 3, 13, (9, 11), (4, 5))
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    _, k_full = fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos)
+    none, k_only = fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos)
+    o_parts = fa.fluxattn_forward_fused_bf16(q, k_only, v, w_q, pos)
+    o_joint = fa.fluxattn_joint_attention_bf16(q, k, v, w_q, w_k, pos)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(k_only.view(torch.int16), k_full.view(torch.int16))
+    assert torch.equal(o_parts.view(torch.int16), o_joint.view(torch.int16))
+    # fp8
+    inp = small(1, 2, 13, (9, 11), None, "fp8", seed=6)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    sq, sk, sv = dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    _, k_full, _, sk_full = fa.fluxattn_qk_norm_rope_fp8(q, k, sq, sk, w_q, w_k, pos)
+    _, k_only, _, sk_only = fa.fluxattn_qk_norm_rope_fp8(None, k, None, sk, None, w_k, pos)
+    o_parts = fa.fluxattn_forward_fused_fp8(q, k_only, v, sq, sk_only, sv, w_q, pos)
+    o_joint = fa.fluxattn_joint_attention_fp8(q, k, v, sq, sk, sv, w_q, w_k, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(k_only.view(torch.uint8), k_full.view(torch.uint8))
+    assert torch.equal(sk_only, sk_full)
+    assert torch.equal(o_parts.view(torch.int16), o_joint.view(torch.int16))
+
+
+def test_joint_fused_bf16_t2i_2048_sampled():
+    _flush("joint fused bf16 t2i_2048_cfg (N=16896, B=2, H=24)")
+    inp = inputs("t2i_2048_cfg")
+    o = fa.fluxattn_joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k),
+                                         dev(inp.pos))
+    torch.cuda.synchronize()
+    heads = [(1, 0), (0, 7)]
+    rows = sample_rows(inp.q.shape[2])
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    rel = check_close(got, joint_ref(inp, heads, rows), BF16_TOL, "joint fused bf16 t2i sampled")
+    assert rel < 1e-2
+
+
+def test_joint_fused_fp8_parity():
+    """fp8 with the fused query prologue; Q' stays in bf16, so the result
+    must also be at least as close as the two-call path (E4M3 Q')."""
+    for inp in (small(1, 2, 64, (16, 16), (8, 8), "fp8"), small(2, 1, 5, (16, 20), None, "fp8", seed=4)):
+        args = (dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale),
+                dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+        o = fa.fluxattn_joint_attention_fp8(*args)
+        o2 = fa.joint_attention_fp8(*args)
+        torch.cuda.synchronize()
+        ref = joint_ref(inp)
+        rel = check_close(f64(o), ref, FP8_TOL, f"joint fused fp8 N={inp.q.shape[2]}")
+        assert rel < 1e-1
+        assert np.abs(f64(o) - ref).mean() <= np.abs(f64(o2) - ref).mean()
+
+
 def test_forward_fp8_parity_tiny_and_ragged():
     for inp in (small(1, 2, 64, (16, 16), None, "fp8"), small(1, 3, 77, (16, 16), None, "fp8", seed=2)):
         o = fa.fluxattn_forward_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale),
@@ -339,4 +436,10 @@ def test_fp8_i2i_2048_sampled():
     torch.cuda.synchronize()
     got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
     rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fp8 i2i sampled")
+    assert rel < 1e-1
+    # the whole block with the fused query prologue
+    o = fa.fluxattn_joint_attention_fp8(q, k, v, sq, sk, sv, dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    torch.cuda.synchronize()
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fused fp8 i2i sampled")
     assert rel < 1e-1
