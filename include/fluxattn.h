@@ -14,7 +14,8 @@
  *     supported attention precision.
  * The pages give no formulas.  This library uses the plain readings:
  *   RMSNorm   y_d = x_d * w_d / sqrt(mean_d(x^2) + eps), one fp32 weight
- *             vector for Q and one for K, shared over batch, heads, streams;
+ *             vector for Q and one for K, shared over batch and heads; the
+ *             _ex entry points take one vector per token stream;
  *   RoPE      head dims split into contiguous (t, h, w) blocks of
  *             (axes_t, axes_h, axes_w); inside axis a's block the adjacent
  *             pair (y[2j], y[2j+1]) = (u, v) is rotated to
@@ -24,8 +25,10 @@
  *
  * Conventions shared by every entry point
  *   Layout     row-major contiguous [B, H, N, D]; element (b,h,n,d) sits at
- *              ((b*H + h)*N + n)*D + d.  pos_ids is int32 [N, 3] = (t, h, w)
- *              per token, shared by all B and H.  Scales are fp32 [B, H].
+ *              ((b*H + h)*N + n)*D + d.  The _ex entry points take strided
+ *              views instead (fluxattn_layout below).  pos_ids is int32
+ *              [N, 3] = (t, h, w) per token, shared by all B and H.  Scales
+ *              are fp32 [B, H], contiguous.
  *   Pointers   all data pointers are DEVICE pointers on the current HIP device.
  *              The caller owns every buffer.  The library keeps no per-call
  *              state, allocates nothing and never synchronises; work is
@@ -57,6 +60,39 @@ extern "C" {
 
 #define FLUXATTN_HEAD_DIM 128
 #define FLUXATTN_MAX_N (1 << 22)
+
+/*
+ * A strided [B, H, N, D] view: element (b,h,n,d) sits at
+ * b*b_stride + h*h_stride + n*n_stride + d elements past the view's pointer
+ * (d is always contiguous).  Contiguous [B,H,N,D] is {H*N*D, N*D, D}; the
+ * [B,N,H,D] layout a QKV projection writes is {N*H*D, D, H*D}; one of q, k,
+ * v inside a packed [B,N,3,H,D] tensor is {3*N*H*D, D, 3*H*D} from that
+ * tensor's pointer plus 0, H*D or 2*H*D elements.
+ * Rules: strides >= 0 and, in bytes, multiples of 16; n_stride >= D (token
+ * rows do not overlap) and at most 2^30 bytes; within one (b,h), row
+ * ceil(N/256)*256 - 1 ends less than 2^32 bytes past row 0.  Outputs must
+ * be one-to-one (no two (b,h,n,d) share an element).  Views whose
+ * bounding ranges overlap are still disjoint when they share all three
+ * strides, b_stride is a multiple of n_stride and they sit in separate
+ * slices of each token row (as the q, k, v slices of a packed tensor do).
+ */
+typedef struct {
+    int64_t b_stride, h_stride, n_stride;
+} fluxattn_layout;
+
+/*
+ * Token streams for per-stream RMSNorm weights: the sequence is the
+ * concatenation of `count` (1..4) streams, stream s holding tokens
+ * [start[s], start[s+1]) (the last runs to N); weight row s applies to
+ * them.  start[0] == 0, starts non-decreasing and <= N (an empty stream is
+ * allowed); entries past count are ignored.  FLUX: text then image (then
+ * reference image) tokens, each stream with its own norm weights (blog post
+ * above, section "Running FLUX 3 inference with TensorRT LLM VisualGen").
+ */
+typedef struct {
+    int32_t count;
+    int32_t start[4];
+} fluxattn_streams;
 
 typedef enum {
     FLUXATTN_OK = 0,
@@ -219,6 +255,70 @@ fluxattn_status fluxattn_joint_attention_fp8(
     uint8_t *k_work, float *k_scale_work, void *o,
     const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
     int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
+
+/*
+ * Strided, multi-stream forms.  Each takes a fluxattn_layout after every
+ * [B,H,N,D] tensor (rules above) and, where norm weights appear, a
+ * fluxattn_streams with q_norm_w / k_norm_w as fp32 [streams.count, D]
+ * (one row per stream).  Everything else, including aliasing (in place
+ * means the same pointer and the same layout), is as in the contiguous
+ * entry point of the same name, which equals its _ex form with contiguous
+ * layouts and one stream.  Invalid layouts or streams give
+ * FLUXATTN_ERR_INVALID_SHAPE.  For the fp8 prologue, q_scale_out /
+ * k_scale_out are sqrt(D) * max|w| / 448 with the maximum over all
+ * streams' rows.  k_work of the joint forms is contiguous [B,H,N,D] and
+ * may equal k only when k is contiguous too.
+ */
+fluxattn_status fluxattn_qk_norm_rope_ex_bf16(
+    const void *q, fluxattn_layout q_layout, const void *k,
+    fluxattn_layout k_layout, void *q_out, fluxattn_layout q_out_layout,
+    void *k_out, fluxattn_layout k_out_layout, const float *q_norm_w,
+    const float *k_norm_w, fluxattn_streams streams, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    void *stream);
+
+fluxattn_status fluxattn_qk_norm_rope_ex_fp8(
+    const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+    fluxattn_layout k_layout, const float *q_scale, const float *k_scale,
+    uint8_t *q_out, fluxattn_layout q_out_layout, uint8_t *k_out,
+    fluxattn_layout k_out_layout, float *q_scale_out, float *k_scale_out,
+    const float *q_norm_w, const float *k_norm_w, fluxattn_streams streams,
+    const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    void *stream);
+
+fluxattn_status fluxattn_forward_ex_bf16(
+    const void *q, fluxattn_layout q_layout, const void *k,
+    fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+    void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
+    int64_t D, float softmax_scale, void *stream);
+
+fluxattn_status fluxattn_forward_ex_fp8(
+    const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+    fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
+    int64_t D, float softmax_scale, void *stream);
+
+fluxattn_status fluxattn_joint_attention_ex_bf16(
+    const void *q, fluxattn_layout q_layout, const void *k,
+    fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+    void *k_work, void *o, fluxattn_layout o_layout, const float *q_norm_w,
+    const float *k_norm_w, fluxattn_streams streams, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, void *stream);
+
+fluxattn_status fluxattn_joint_attention_ex_fp8(
+    const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+    fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    uint8_t *k_work, float *k_scale_work, void *o, fluxattn_layout o_layout,
+    const float *q_norm_w, const float *k_norm_w, fluxattn_streams streams,
+    const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
     int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
     float softmax_scale, void *stream);
 

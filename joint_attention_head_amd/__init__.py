@@ -16,6 +16,11 @@ Entry points (same names as the C ABI):
     fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos_ids, ...)
     fluxattn_joint_attention_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, ...)
     fluxattn_joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids, ...)
+and the strided, multi-stream forms fluxattn_qk_norm_rope_ex_{bf16,fp8},
+fluxattn_forward_ex_{bf16,fp8} and fluxattn_joint_attention_ex_{bf16,fp8},
+which accept any [B,H,N,D] tensor view whose last dimension is contiguous
+(for example q, k, v sliced out of a packed [B,N,3,H,D] projection output)
+and per-stream norm weights [S, D] with the streams' first tokens.
 """
 from __future__ import annotations
 
@@ -50,6 +55,12 @@ EXPORTS = (
     "fluxattn_forward_fused_fp8",
     "fluxattn_joint_attention_bf16",
     "fluxattn_joint_attention_fp8",
+    "fluxattn_qk_norm_rope_ex_bf16",
+    "fluxattn_qk_norm_rope_ex_fp8",
+    "fluxattn_forward_ex_bf16",
+    "fluxattn_forward_ex_fp8",
+    "fluxattn_joint_attention_ex_bf16",
+    "fluxattn_joint_attention_ex_fp8",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
     "fluxattn_version",
@@ -70,6 +81,21 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 _f = ctypes.c_float
 
+
+
+class Layout(ctypes.Structure):
+    """fluxattn_layout: element strides of a [B,H,N,D] view (d contiguous)."""
+    _fields_ = [("b_stride", ctypes.c_int64), ("h_stride", ctypes.c_int64), ("n_stride", ctypes.c_int64)]
+
+
+class Streams(ctypes.Structure):
+    """fluxattn_streams: 1..4 token streams given by their first tokens."""
+    _fields_ = [("count", ctypes.c_int32), ("start", ctypes.c_int32 * 4)]
+
+
+_L = Layout
+_S = Streams
+
 _SIGS = {
     "fluxattn_qk_norm_rope_bf16": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64,
                                    _i32, _i32, _i32, _f, _f, _p],
@@ -85,6 +111,16 @@ _SIGS = {
                                       _i32, _i32, _i32, _f, _f, _f, _p],
     "fluxattn_joint_attention_fp8": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
                                      _i64, _i32, _i32, _i32, _f, _f, _f, _p],
+    "fluxattn_qk_norm_rope_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _p, _p, _S, _p, _i64, _i64, _i64, _i64,
+                                      _i32, _i32, _i32, _f, _f, _p],
+    "fluxattn_qk_norm_rope_ex_fp8": [_p, _L, _p, _L, _p, _p, _p, _L, _p, _L, _p, _p, _p, _p, _S, _p, _i64, _i64,
+                                     _i64, _i64, _i32, _i32, _i32, _f, _f, _p],
+    "fluxattn_forward_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _i64, _i64, _i64, _i64, _f, _p],
+    "fluxattn_forward_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _L, _i64, _i64, _i64, _i64, _f, _p],
+    "fluxattn_joint_attention_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _p, _L, _p, _p, _S, _p, _i64, _i64, _i64,
+                                         _i64, _i32, _i32, _i32, _f, _f, _f, _p],
+    "fluxattn_joint_attention_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _p, _p, _L, _p, _p, _S, _p,
+                                        _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _p],
 }
 
 
@@ -340,4 +376,203 @@ def fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos
         q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
         v_scale.data_ptr(), o.data_ptr(), q_norm_w.data_ptr(), pos_ids.data_ptr(), B, H, N, D, axes[0],
         axes[1], axes[2], float(theta), float(eps), float(softmax_scale), _stream(stream)))
+    return o
+
+
+# ---- strided views and token streams
+
+
+def layout_of(t: torch.Tensor) -> Layout:
+    """The fluxattn_layout of a [B,H,N,D] tensor view (element strides)."""
+    sb, sh, sn, sd = t.stride()
+    if sd != 1 and t.shape[3] != 1:
+        raise ValueError("the head dimension of a view must be contiguous")
+    return Layout(sb, sh, sn)
+
+
+def streams_of(starts) -> Streams:
+    """fluxattn_streams from the first token of each stream, e.g. (0, 512)
+    for 512 text tokens followed by the image tokens."""
+    starts = [int(x) for x in starts]
+    if not 1 <= len(starts) <= 4:
+        raise ValueError("1 to 4 token streams")
+    st = Streams()
+    st.count = len(starts)
+    for i, x in enumerate(starts):
+        st.start[i] = x
+    return st
+
+
+def _need_view(t, name: str, dtype, shape):
+    """Like _need for a strided [B,H,N,D] view; returns its layout."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return layout_of(t)
+
+
+def _weights(w, name, n_streams, D):
+    _need(w, name, torch.float32)
+    if w.dim() == 1 and n_streams == 1:
+        w = w.view(1, D)
+    if tuple(w.shape) != (n_streams, D):
+        raise ValueError(f"{name} must have shape ({n_streams}, {D}), got {tuple(w.shape)}")
+    return w
+
+
+def fluxattn_qk_norm_rope_ex_bf16(q, k, q_norm_w, k_norm_w, pos_ids, streams=(0,), q_out=None, k_out=None,
+                                  axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, stream=None):
+    """RMSNorm + RoPE of bf16 [B,H,N,D] views with one weight row per token
+    stream (q_norm_w, k_norm_w: [S, D]; streams: the S first tokens).
+    Outputs default to new contiguous tensors; pass q_out=q, k_out=k to work
+    in place.  q=None processes the keys only.  Returns (q_out, k_out)."""
+    shape = tuple(k.shape)
+    B, H, N, D = _bhnd(k)
+    st = streams_of(streams)
+    lk = _need_view(k, "k", torch.bfloat16, shape)
+    k_norm_w = _weights(k_norm_w, "k_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    k_out = torch.empty(shape, dtype=k.dtype, device=k.device) if k_out is None else k_out
+    lko = _need_view(k_out, "k_out", torch.bfloat16, shape)
+    lq = lqo = Layout(0, 0, 0)
+    if q is not None:
+        lq = _need_view(q, "q", torch.bfloat16, shape)
+        q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+        q_out = torch.empty(shape, dtype=q.dtype, device=q.device) if q_out is None else q_out
+        lqo = _need_view(q_out, "q_out", torch.bfloat16, shape)
+    else:
+        q_out, q_norm_w = None, None
+    _check(lib().fluxattn_qk_norm_rope_ex_bf16(
+        _ptr(q), lq, k.data_ptr(), lk, _ptr(q_out), lqo, k_out.data_ptr(), lko, _ptr(q_norm_w),
+        k_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta),
+        float(eps), _stream(stream)))
+    return q_out, k_out
+
+
+def fluxattn_qk_norm_rope_ex_fp8(q, k, q_scale, k_scale, q_norm_w, k_norm_w, pos_ids, streams=(0,),
+                                 q_out=None, k_out=None, q_scale_out=None, k_scale_out=None,
+                                 axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, stream=None):
+    """fp8 form of fluxattn_qk_norm_rope_ex_bf16; returns (q_out, k_out,
+    q_scale_out, k_scale_out)."""
+    shape = tuple(k.shape)
+    B, H, N, D = _bhnd(k)
+    e4 = torch.float8_e4m3fn
+    st = streams_of(streams)
+    lk = _need_view(k, "k", e4, shape)
+    _need(k_scale, "k_scale", torch.float32, (B, H))
+    k_norm_w = _weights(k_norm_w, "k_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    k_out = torch.empty(shape, dtype=e4, device=k.device) if k_out is None else k_out
+    lko = _need_view(k_out, "k_out", e4, shape)
+    k_scale_out = torch.empty_like(k_scale) if k_scale_out is None else k_scale_out
+    _need(k_scale_out, "k_scale_out", torch.float32, (B, H))
+    lq = lqo = Layout(0, 0, 0)
+    if q is not None:
+        lq = _need_view(q, "q", e4, shape)
+        _need(q_scale, "q_scale", torch.float32, (B, H))
+        q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+        q_out = torch.empty(shape, dtype=e4, device=q.device) if q_out is None else q_out
+        lqo = _need_view(q_out, "q_out", e4, shape)
+        q_scale_out = torch.empty_like(q_scale) if q_scale_out is None else q_scale_out
+        _need(q_scale_out, "q_scale_out", torch.float32, (B, H))
+    else:
+        q_scale, q_out, q_scale_out, q_norm_w = None, None, None, None
+    _check(lib().fluxattn_qk_norm_rope_ex_fp8(
+        _ptr(q), lq, k.data_ptr(), lk, _ptr(q_scale), k_scale.data_ptr(), _ptr(q_out), lqo, k_out.data_ptr(),
+        lko, _ptr(q_scale_out), k_scale_out.data_ptr(), _ptr(q_norm_w), k_norm_w.data_ptr(), st,
+        pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps), _stream(stream)))
+    return q_out, k_out, q_scale_out, k_scale_out
+
+
+def fluxattn_forward_ex_bf16(q, k, v, o=None, softmax_scale=0.0, stream=None):
+    """Attention on bf16 [B,H,N,D] views; o defaults to a new contiguous
+    tensor.  Returns o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    lq = _need_view(q, "q", torch.bfloat16, shape)
+    lk = _need_view(k, "k", torch.bfloat16, shape)
+    lv = _need_view(v, "v", torch.bfloat16, shape)
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    _check(lib().fluxattn_forward_ex_bf16(q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, o.data_ptr(),
+                                          lo, B, H, N, D, float(softmax_scale), _stream(stream)))
+    return o
+
+
+def fluxattn_forward_ex_fp8(q, k, v, q_scale, k_scale, v_scale, o=None, softmax_scale=0.0, stream=None):
+    """fp8 form of fluxattn_forward_ex_bf16 (fp32 [B,H] scales); bf16 o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    e4 = torch.float8_e4m3fn
+    lq = _need_view(q, "q", e4, shape)
+    lk = _need_view(k, "k", e4, shape)
+    lv = _need_view(v, "v", e4, shape)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, (B, H))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    _check(lib().fluxattn_forward_ex_fp8(q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(),
+                                         k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lo, B, H, N, D,
+                                         float(softmax_scale), _stream(stream)))
+    return o
+
+
+def fluxattn_joint_attention_ex_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, streams=(0,), o=None,
+                                     k_work=None, axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS,
+                                     softmax_scale=0.0, stream=None):
+    """The whole block on raw bf16 [B,H,N,D] views with per-stream norm
+    weights [S, D].  k_work (contiguous [B,H,N,D]) receives K'; o defaults
+    to a new contiguous tensor.  Returns o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    st = streams_of(streams)
+    lq = _need_view(q, "q", torch.bfloat16, shape)
+    lk = _need_view(k, "k", torch.bfloat16, shape)
+    lv = _need_view(v, "v", torch.bfloat16, shape)
+    q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+    k_norm_w = _weights(k_norm_w, "k_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    k_work = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if k_work is None else k_work
+    _need(k_work, "k_work", torch.bfloat16, shape)
+    _check(lib().fluxattn_joint_attention_ex_bf16(
+        q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, k_work.data_ptr(), o.data_ptr(), lo,
+        q_norm_w.data_ptr(), k_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1],
+        axes[2], float(theta), float(eps), float(softmax_scale), _stream(stream)))
+    return o
+
+
+def fluxattn_joint_attention_ex_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids,
+                                    streams=(0,), o=None, k_work=None, k_scale_work=None, axes=ROPE_AXES,
+                                    theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, stream=None):
+    """fp8 form of fluxattn_joint_attention_ex_bf16; returns bf16 o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    e4 = torch.float8_e4m3fn
+    st = streams_of(streams)
+    lq = _need_view(q, "q", e4, shape)
+    lk = _need_view(k, "k", e4, shape)
+    lv = _need_view(v, "v", e4, shape)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, (B, H))
+    q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+    k_norm_w = _weights(k_norm_w, "k_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    k_work = torch.empty(shape, dtype=e4, device=q.device) if k_work is None else k_work
+    _need(k_work, "k_work", e4, shape)
+    k_scale_work = torch.empty_like(k_scale) if k_scale_work is None else k_scale_work
+    _need(k_scale_work, "k_scale_work", torch.float32, (B, H))
+    _check(lib().fluxattn_joint_attention_ex_fp8(
+        q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), k_work.data_ptr(), k_scale_work.data_ptr(), o.data_ptr(), lo, q_norm_w.data_ptr(),
+        k_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta),
+        float(eps), float(softmax_scale), _stream(stream)))
     return o

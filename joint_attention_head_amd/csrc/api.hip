@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "fluxattn.h"
@@ -26,19 +27,13 @@ struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
 Range span(const void *p, int64_t bytes) {
+  if (!p) return {0, 0};
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
   return {lo, lo + static_cast<uintptr_t>(bytes)};
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// An output must either coincide exactly with its own input (in place) or
-// overlap nothing else.
-bool output_ok(Range out, Range own_in, const Range *others, int n_others) {
-  if (overlap(out, own_in) && !(out.lo == own_in.lo && out.hi == own_in.hi)) return false;
-  for (int i = 0; i < n_others; ++i)
-    if (overlap(out, others[i])) return false;
-  return true;
-}
+// ---- shapes and parameters
 
 bool shape_ok(int64_t B, int64_t H, int64_t N, int64_t D) {
   if (B < 1 || H < 1 || N < 1 || D != kHeadDim) return false;
@@ -59,6 +54,102 @@ bool rope_ok(int32_t at, int32_t ah, int32_t aw, float theta, float eps) {
   if (!(theta > 0.f) || !isfinite(theta)) return false;
   if (!(eps >= 0.f) || !isfinite(eps)) return false;
   return true;
+}
+
+bool scale_ok(float softmax_scale) {
+  return softmax_scale <= 0.f || (softmax_scale > 0.f && isfinite(softmax_scale));  // rejects NaN, +inf
+}
+
+// Norm-weight streams: 1..4 token ranges starting at 0, non-decreasing
+// starts within [0, N].
+bool streams_ok(const fluxattn_streams &s, int64_t N) {
+  if (s.count < 1 || s.count > 4 || s.start[0] != 0) return false;
+  for (int i = 1; i < s.count; ++i)
+    if (s.start[i] < s.start[i - 1] || s.start[i] > N) return false;
+  return true;
+}
+
+Streams to_streams(const fluxattn_streams &s) {
+  Streams r;
+  for (int i = 0; i < 4; ++i) r.start[i] = i < s.count ? s.start[i] : 0x7fffffff;
+  return r;
+}
+
+// ---- strided [B, H, N, D] views (d contiguous)
+
+struct View {
+  const void *p;
+  int64_t sb, sh, sn;  // element strides
+};
+
+View contiguous(const void *p, int64_t H, int64_t N, int64_t D) { return {p, H * N * D, N * D, D}; }
+View view_of(const void *p, const fluxattn_layout &l) { return {p, l.b_stride, l.h_stride, l.n_stride}; }
+
+bool is_contiguous(const View &v, int64_t H, int64_t N, int64_t D) {
+  return v.sb == H * N * D && v.sh == N * D && v.sn == D;
+}
+
+// Strides are non-negative and keep every row 16-byte aligned; token rows
+// do not overlap (rows past N then lie past a head's last row, where the
+// attention kernel's bounded loads read zeros and its stores drop) and the
+// token stride fits the kernels' 32-bit row pitch.
+bool strides_ok(const View &v, int64_t D, int esize) {
+  if (v.sb < 0 || v.sh < 0 || v.sn < D) return false;
+  if ((v.sb * esize) % 16 || (v.sh * esize) % 16 || (v.sn * esize) % 16) return false;
+  return v.sn * esize <= (int64_t(1) << 30);
+}
+
+// Elements from a view's first to past its last element.
+int64_t extent_elems(const View &v, int64_t B, int64_t H, int64_t N, int64_t D) {
+  return (B - 1) * v.sb + (H - 1) * v.sh + (N - 1) * v.sn + D;
+}
+Range extent(const View &v, int64_t B, int64_t H, int64_t N, int64_t D, int esize) {
+  return span(v.p, extent_elems(v, B, H, N, D) * esize);
+}
+
+// The attention kernel addresses a head through 32-bit buffer offsets and
+// walks query rows in blocks of 256: every row of the last block, padded
+// past N, must still have an offset below 2^32 so that no offset wraps back
+// into the head.
+bool head_fits(const View &v, int64_t N, int64_t D, int esize) {
+  const int64_t rows = (N + 255) / 256 * 256;
+  return ((rows - 1) * v.sn + D) * esize < (int64_t(1) << 32);
+}
+
+// Distinct (b, h, n, d) reach distinct elements (needed for outputs).
+bool injective(const View &v, int64_t B, int64_t H, int64_t N, int64_t D) {
+  struct Dim {
+    int64_t stride, count;
+  } dims[3] = {{v.sb, B}, {v.sh, H}, {v.sn, N}};
+  std::sort(dims, dims + 3, [](const Dim &a, const Dim &b) { return a.stride < b.stride; });
+  int64_t need = D;  // the next dimension must step past everything before it
+  for (const Dim &d : dims) {
+    if (d.count == 1) continue;
+    if (d.stride < need) return false;
+    need = d.stride * d.count;
+  }
+  return true;
+}
+
+bool same_view(const View &a, const View &b) {
+  return a.p == b.p && a.sb == b.sb && a.sh == b.sh && a.sn == b.sn;
+}
+
+// No element in common.  Views whose extents overlap are still disjoint if
+// they share strides and interleave inside token rows, like the q, k and v
+// views of a packed [B, N, 3, H, D] tensor.
+bool disjoint(const View &a, const View &b, int64_t B, int64_t H, int64_t N, int64_t D, int esize) {
+  if (!a.p || !b.p) return true;
+  if (!overlap(extent(a, B, H, N, D, esize), extent(b, B, H, N, D, esize))) return true;
+  if (a.sb != b.sb || a.sh != b.sh || a.sn != b.sn) return false;
+  const int64_t diff = static_cast<int64_t>(reinterpret_cast<uintptr_t>(b.p) - reinterpret_cast<uintptr_t>(a.p));
+  if (diff % esize) return false;
+  const int64_t delta = diff / esize;
+  const int64_t foot = (H - 1) * a.sh + D;  // elements of one token row of a view
+  if (a.sn < foot) return false;
+  if (B > 1 && a.sb % a.sn) return false;
+  const int64_t r = ((delta % a.sn) + a.sn) % a.sn;
+  return r >= foot && r + foot <= a.sn;
 }
 
 // gfx950 check, cached per device (arch never changes for a device id).
@@ -96,22 +187,43 @@ RopeTable make_rope_table(int32_t at, int32_t ah, int32_t aw, float theta) {
   return t;
 }
 
+// A buffer that is not a [B,H,N,D] view (weights, ids, scales), as a view
+// whose single row spans it: disjoint() then compares extents only.
+struct Plain {
+  const void *p;
+  int64_t bytes;
+};
+
+bool apart(const View &v, int64_t B, int64_t H, int64_t N, int64_t D, int esize, const Plain *plains, int n) {
+  const Range r = extent(v, B, H, N, D, esize);
+  for (int i = 0; i < n; ++i)
+    if (overlap(r, span(plains[i].p, plains[i].bytes))) return false;
+  return true;
+}
+
+// ---- the prologue: RMSNorm + RoPE of q and k views (q may be absent)
+
 template <bool FP8>
-fluxattn_status prologue_impl(const void *q, const void *k, const float *q_scale, const float *k_scale,
-                              void *q_out, void *k_out, float *q_scale_out, float *k_scale_out,
-                              const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
-                              int64_t B, int64_t H, int64_t N, int64_t D, int32_t at, int32_t ah,
-                              int32_t aw, float theta, float eps, void *stream) {
+fluxattn_status prologue_core(View q, View k, const float *q_scale, const float *k_scale, View qo, View ko,
+                              float *q_scale_out, float *k_scale_out, const float *q_norm_w,
+                              const float *k_norm_w, const fluxattn_streams &streams, const int32_t *pos_ids,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int32_t at, int32_t ah, int32_t aw,
+                              float theta, float eps, void *stream) {
+  constexpr int E = FP8 ? 1 : 2;
   // q == NULL: keys only (q_out, q_norm_w and the fp8 q scales must then be NULL too)
-  const bool has_q = q != nullptr;
-  if (!has_q && (q_out || q_norm_w || (FP8 && (q_scale || q_scale_out)))) return FLUXATTN_ERR_NULL_POINTER;
-  if (!k || !k_out || !k_norm_w || !pos_ids) return FLUXATTN_ERR_NULL_POINTER;
-  if (has_q && (!q_out || !q_norm_w)) return FLUXATTN_ERR_NULL_POINTER;
+  const bool has_q = q.p != nullptr;
+  if (!has_q && (qo.p || q_norm_w || (FP8 && (q_scale || q_scale_out)))) return FLUXATTN_ERR_NULL_POINTER;
+  if (!k.p || !ko.p || !k_norm_w || !pos_ids) return FLUXATTN_ERR_NULL_POINTER;
+  if (has_q && (!qo.p || !q_norm_w)) return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!k_scale || !k_scale_out)) return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && has_q && (!q_scale || !q_scale_out)) return FLUXATTN_ERR_NULL_POINTER;
-  if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps) || !streams_ok(streams, N))
+    return FLUXATTN_ERR_INVALID_SHAPE;
+  for (const View *v : {&q, &k, &qo, &ko})
+    if (v->p && (!strides_ok(*v, D, E) || !head_fits(*v, N, D, E))) return FLUXATTN_ERR_INVALID_SHAPE;
+  if ((has_q && !injective(qo, B, H, N, D)) || !injective(ko, B, H, N, D)) return FLUXATTN_ERR_INVALID_SHAPE;
   // (aligned() of a NULL pointer holds)
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
+  if (!aligned(q.p, 16) || !aligned(k.p, 16) || !aligned(qo.p, 16) || !aligned(ko.p, 16) ||
       !aligned(q_norm_w, 4) || !aligned(k_norm_w, 4) || !aligned(pos_ids, 4))
     return FLUXATTN_ERR_MISALIGNED;
   if (FP8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(q_scale_out, 4) ||
@@ -119,39 +231,40 @@ fluxattn_status prologue_impl(const void *q, const void *k, const float *q_scale
     return FLUXATTN_ERR_MISALIGNED;
 
   const int64_t BH = B * H;
-  const int64_t tensor_bytes = BH * N * D * (FP8 ? 1 : 2);
-  const Range none = {0, 0};
-  auto sp = [](const void *p, int64_t bytes) { return p ? span(p, bytes) : Range{0, 0}; };
-  const Range rq = sp(q, tensor_bytes), rk = span(k, tensor_bytes);
-  const Range rqo = sp(q_out, tensor_bytes), rko = span(k_out, tensor_bytes);
-  const Range rwq = sp(q_norm_w, D * 4), rwk = span(k_norm_w, D * 4), rp = span(pos_ids, N * 12);
-  Range rsq = none, rsk = none, rsqo = none, rsko = none;
-  if (FP8) {
-    rsq = sp(q_scale, BH * 4);
-    rsk = span(k_scale, BH * 4);
-    rsqo = sp(q_scale_out, BH * 4);
-    rsko = span(k_scale_out, BH * 4);
+  const int64_t S = streams.count;
+  const Plain plains[] = {{q_norm_w, S * D * 4}, {k_norm_w, S * D * 4}, {pos_ids, N * 12}, {q_scale, BH * 4},
+                          {k_scale, BH * 4},     {q_scale_out, BH * 4}, {k_scale_out, BH * 4}};
+  // outputs: exactly their own input (in place) or apart from it; apart from
+  // the other tensors and every plain buffer (a scale output is checked
+  // against all others but itself)
+  if (has_q) {
+    if (!same_view(qo, q) && !disjoint(qo, q, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+    if (!disjoint(qo, k, B, H, N, D, E) || !disjoint(qo, ko, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+    if (!apart(qo, B, H, N, D, E, plains, 7)) return FLUXATTN_ERR_ALIASING;
   }
-  {
-    const Range oq[] = {rk, rko, rwq, rwk, rp, rsq, rsk, rsqo, rsko};
-    const Range ok[] = {rq, rqo, rwq, rwk, rp, rsq, rsk, rsqo, rsko};
-    if ((has_q && !output_ok(rqo, rq, oq, FP8 ? 9 : 5)) || !output_ok(rko, rk, ok, FP8 ? 9 : 5))
-      return FLUXATTN_ERR_ALIASING;
-    if (FP8) {
-      const Range os[] = {rq, rk, rqo, rko, rwq, rwk, rp, rsq, rsk, rsko};
-      const Range ok2[] = {rq, rk, rqo, rko, rwq, rwk, rp, rsq, rsk, rsqo};
-      if ((has_q && !output_ok(rsqo, none, os, 10)) || !output_ok(rsko, none, ok2, 10))
-        return FLUXATTN_ERR_ALIASING;
+  if (!same_view(ko, k) && !disjoint(ko, k, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+  if (!disjoint(ko, q, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+  if (!apart(ko, B, H, N, D, E, plains, 7)) return FLUXATTN_ERR_ALIASING;
+  if (FP8) {
+    const Range tensors[] = {extent(q, B, H, N, D, E), extent(k, B, H, N, D, E), extent(qo, B, H, N, D, E),
+                             extent(ko, B, H, N, D, E)};
+    for (int o = 5; o < 7; ++o) {
+      if (!plains[o].p) continue;
+      const Range r = span(plains[o].p, plains[o].bytes);
+      for (const Range &t : tensors)
+        if (overlap(r, t)) return FLUXATTN_ERR_ALIASING;
+      for (int i = 0; i < 7; ++i)
+        if (i != o && overlap(r, span(plains[i].p, plains[i].bytes))) return FLUXATTN_ERR_ALIASING;
     }
   }
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
 
   PrologueArgs a{};
-  a.q = q;
-  a.k = k;
-  a.q_out = q_out;
-  a.k_out = k_out;
+  a.q = q.p;
+  a.k = k.p;
+  a.q_out = const_cast<void *>(qo.p);
+  a.k_out = const_cast<void *>(ko.p);
   a.w_q = q_norm_w;
   a.w_k = k_norm_w;
   a.pos = pos_ids;
@@ -160,164 +273,152 @@ fluxattn_status prologue_impl(const void *q, const void *k, const float *q_scale
   a.q_scale_out = q_scale_out;
   a.k_scale_out = k_scale_out;
   a.BH = BH;
+  a.H = static_cast<int32_t>(H);
   a.N = static_cast<int32_t>(N);
   a.eps = eps;
+  auto st = [](const View &v) { return Strides{v.sb, v.sh, static_cast<int32_t>(v.sn)}; };
+  a.sq = st(q);
+  a.sk = st(k);
+  a.sqo = st(qo);
+  a.sko = st(ko);
+  a.streams = to_streams(streams);
+  a.num_streams = streams.count;
   const RopeTable t = make_rope_table(at, ah, aw, theta);
   const hipError_t e = FP8 ? launch_prologue_fp8(a, t, static_cast<hipStream_t>(stream))
                            : launch_prologue_bf16(a, t, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
 }
 
-template <bool FP8>
-fluxattn_status forward_impl(const void *q, const void *k, const void *v, const float *q_scale,
-                             const float *k_scale, const float *v_scale, void *o, int64_t B, int64_t H,
-                             int64_t N, int64_t D, float softmax_scale, void *stream) {
-  if (!q || !k || !v || !o) return FLUXATTN_ERR_NULL_POINTER;
-  if (FP8 && (!q_scale || !k_scale || !v_scale)) return FLUXATTN_ERR_NULL_POINTER;
-  if (!shape_ok(B, H, N, D)) return FLUXATTN_ERR_INVALID_SHAPE;
-  if (!(softmax_scale <= 0.f) && !(softmax_scale > 0.f && isfinite(softmax_scale)))
-    return FLUXATTN_ERR_INVALID_SHAPE;  // NaN or +inf
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FLUXATTN_ERR_MISALIGNED;
-  if (FP8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
-    return FLUXATTN_ERR_MISALIGNED;
-  const int64_t BH = B * H;
-  const int64_t in_bytes = BH * N * D * (FP8 ? 1 : 2);
-  const Range ro = span(o, BH * N * D * 2);
-  const Range none = {0, 0};
-  Range others[6] = {span(q, in_bytes), span(k, in_bytes), span(v, in_bytes), none, none, none};
-  if (FP8) {
-    others[3] = span(q_scale, BH * 4);
-    others[4] = span(k_scale, BH * 4);
-    others[5] = span(v_scale, BH * 4);
-  }
-  if (!output_ok(ro, none, others, FP8 ? 6 : 3)) return FLUXATTN_ERR_ALIASING;
-  const fluxattn_status dev = device_ok();
-  if (dev != FLUXATTN_OK) return dev;
+// ---- attention (fused: q is raw and gets RMSNorm + RoPE on load)
 
-  const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / sqrt(static_cast<double>(D));
-  ForwardArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.q_scale = q_scale;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.BH = static_cast<int32_t>(BH);
-  a.N = static_cast<int32_t>(N);
-  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);  // * log2(e)
-  const hipError_t e = FP8 ? launch_forward_fp8(a, static_cast<hipStream_t>(stream))
-                           : launch_forward_bf16(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
-}
-
-// Attention whose Q load normalises and rotates raw queries (K already
-// prepared).
 template <bool FP8>
-fluxattn_status fused_impl(const void *q, const void *k, const void *v, const float *q_scale,
-                           const float *k_scale, const float *v_scale, void *o, const float *q_norm_w,
-                           const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D, int32_t at,
-                           int32_t ah, int32_t aw, float theta, float eps, float softmax_scale, void *stream) {
-  if (!q || !k || !v || !o || !q_norm_w || !pos_ids) return FLUXATTN_ERR_NULL_POINTER;
+fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const float *k_scale,
+                             const float *v_scale, View o, int64_t B, int64_t H, int64_t N, int64_t D,
+                             float softmax_scale, bool fused, const float *q_norm_w,
+                             const fluxattn_streams &streams, const int32_t *pos_ids, int32_t at, int32_t ah,
+                             int32_t aw, float theta, float eps, void *stream) {
+  constexpr int E = FP8 ? 1 : 2;
+  if (!q.p || !k.p || !v.p || !o.p) return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!q_scale || !k_scale || !v_scale)) return FLUXATTN_ERR_NULL_POINTER;
-  if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps)) return FLUXATTN_ERR_INVALID_SHAPE;
-  if (!(softmax_scale <= 0.f) && !(softmax_scale > 0.f && isfinite(softmax_scale)))
-    return FLUXATTN_ERR_INVALID_SHAPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(q_norm_w, 16) ||
-      !aligned(pos_ids, 4))
+  if (fused && (!q_norm_w || !pos_ids)) return FLUXATTN_ERR_NULL_POINTER;
+  if (!shape_ok(B, H, N, D) || !scale_ok(softmax_scale)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (fused && (!rope_ok(at, ah, aw, theta, eps) || !streams_ok(streams, N))) return FLUXATTN_ERR_INVALID_SHAPE;
+  for (const View *w : {&q, &k, &v})
+    if (!strides_ok(*w, D, E) || !head_fits(*w, N, D, E)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!strides_ok(o, D, 2) || !head_fits(o, N, D, 2) || !injective(o, B, H, N, D)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!aligned(q.p, 16) || !aligned(k.p, 16) || !aligned(v.p, 16) || !aligned(o.p, 16))
     return FLUXATTN_ERR_MISALIGNED;
   if (FP8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))) return FLUXATTN_ERR_MISALIGNED;
+  if (fused && (!aligned(q_norm_w, 16) || !aligned(pos_ids, 4))) return FLUXATTN_ERR_MISALIGNED;
   const int64_t BH = B * H;
-  const int64_t in_bytes = BH * N * D * (FP8 ? 1 : 2);
-  const Range none = {0, 0};
-  Range others[8] = {span(q, in_bytes), span(k, in_bytes), span(v, in_bytes), span(q_norm_w, D * 4),
-                     span(pos_ids, N * 12), none, none, none};
-  if (FP8) {
-    others[5] = span(q_scale, BH * 4);
-    others[6] = span(k_scale, BH * 4);
-    others[7] = span(v_scale, BH * 4);
+  const Range ro = extent(o, B, H, N, D, 2);
+  for (const View *w : {&q, &k, &v})
+    if (overlap(ro, extent(*w, B, H, N, D, E))) return FLUXATTN_ERR_ALIASING;
+  {
+    const Plain plains[] = {{q_scale, BH * 4}, {k_scale, BH * 4}, {v_scale, BH * 4},
+                            {fused ? q_norm_w : nullptr, streams.count * D * 4}, {fused ? pos_ids : nullptr, N * 12}};
+    if (!apart(o, B, H, N, D, 2, plains, 5)) return FLUXATTN_ERR_ALIASING;
   }
-  if (!output_ok(span(o, BH * N * D * 2), none, others, 8)) return FLUXATTN_ERR_ALIASING;
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
 
   const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / sqrt(static_cast<double>(D));
   ForwardArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
+  a.q = q.p;
+  a.k = k.p;
+  a.v = v.p;
+  a.o = const_cast<void *>(o.p);
   a.q_scale = q_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.BH = static_cast<int32_t>(BH);
+  a.H = static_cast<int32_t>(H);
   a.N = static_cast<int32_t>(N);
-  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
-  a.w_q = q_norm_w;
-  a.pos = pos_ids;
-  a.eps = eps;
-  const int32_t dims[3] = {at, ah, aw};
-  a.rope_first[0] = 0;
-  for (int i = 0; i < 3; ++i) {
-    a.rope_first[i + 1] = a.rope_first[i] + dims[i] / 2;
-    a.rope_log2_step[i] = dims[i] > 0 ? static_cast<float>(-2.0 * log2(static_cast<double>(theta)) / dims[i]) : 0.f;
+  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);  // * log2(e)
+  auto st = [](const View &w) { return Strides{w.sb, w.sh, static_cast<int32_t>(w.sn)}; };
+  a.sq = st(q);
+  a.sk = st(k);
+  a.sv = st(v);
+  a.so = st(o);
+  if (fused) {
+    a.w_q = q_norm_w;
+    a.pos = pos_ids;
+    a.eps = eps;
+    a.streams = to_streams(streams);
+    const int32_t dims[3] = {at, ah, aw};
+    a.rope_first[0] = 0;
+    for (int i = 0; i < 3; ++i) {
+      a.rope_first[i + 1] = a.rope_first[i] + dims[i] / 2;
+      a.rope_log2_step[i] =
+          dims[i] > 0 ? static_cast<float>(-2.0 * log2(static_cast<double>(theta)) / dims[i]) : 0.f;
+    }
   }
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = FP8 ? launch_forward_fused_fp8(a, st) : launch_forward_fused_bf16(a, st);
+  const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
+                         is_contiguous(o, H, N, D));
+  const hipError_t e = launch_forward(a, FP8, fused, strided, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
 }
 
-// The whole block: keys' prologue into k_work, then the fused attention.
+// ---- the whole block: keys-only prologue into k_work (contiguous), then
+// the fused attention
+
 template <bool FP8>
-fluxattn_status joint_impl(const void *q, const void *k, const void *v, const float *q_scale,
-                           const float *k_scale, const float *v_scale, void *k_work, float *k_scale_work,
-                           void *o, const float *q_norm_w, const float *k_norm_w, const int32_t *pos_ids,
-                           int64_t B, int64_t H, int64_t N, int64_t D, int32_t at, int32_t ah, int32_t aw,
-                           float theta, float eps, float softmax_scale, void *stream) {
-  if (!q || !k || !v || !k_work || !o || !q_norm_w || !k_norm_w || !pos_ids) return FLUXATTN_ERR_NULL_POINTER;
+fluxattn_status joint_core(View q, View k, View v, const float *q_scale, const float *k_scale,
+                           const float *v_scale, void *k_work, float *k_scale_work, View o,
+                           const float *q_norm_w, const float *k_norm_w, const fluxattn_streams &streams,
+                           const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D, int32_t at,
+                           int32_t ah, int32_t aw, float theta, float eps, float softmax_scale, void *stream) {
+  constexpr int E = FP8 ? 1 : 2;
+  if (!q.p || !k.p || !v.p || !k_work || !o.p || !q_norm_w || !k_norm_w || !pos_ids)
+    return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!q_scale || !k_scale || !v_scale || !k_scale_work)) return FLUXATTN_ERR_NULL_POINTER;
-  if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps)) return FLUXATTN_ERR_INVALID_SHAPE;
-  if (!(softmax_scale <= 0.f) && !(softmax_scale > 0.f && isfinite(softmax_scale)))
+  if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps) || !scale_ok(softmax_scale) ||
+      !streams_ok(streams, N))
     return FLUXATTN_ERR_INVALID_SHAPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_work, 16) || !aligned(o, 16) ||
+  View kw = contiguous(k_work, H, N, D);
+  for (const View *w : {&q, &k, &v})
+    if (!strides_ok(*w, D, E) || !head_fits(*w, N, D, E)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!strides_ok(o, D, 2) || !head_fits(o, N, D, 2) || !injective(o, B, H, N, D) || !head_fits(kw, N, D, E))
+    return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!aligned(q.p, 16) || !aligned(k.p, 16) || !aligned(v.p, 16) || !aligned(k_work, 16) || !aligned(o.p, 16) ||
       !aligned(q_norm_w, 16) || !aligned(k_norm_w, 4) || !aligned(pos_ids, 4))
     return FLUXATTN_ERR_MISALIGNED;
   if (FP8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(k_scale_work, 4)))
     return FLUXATTN_ERR_MISALIGNED;
 
   const int64_t BH = B * H;
-  const int64_t in_bytes = BH * N * D * (FP8 ? 1 : 2);
-  const Range none = {0, 0};
-  const Range rq = span(q, in_bytes), rk = span(k, in_bytes), rv = span(v, in_bytes);
-  const Range rkw = span(k_work, in_bytes), ro = span(o, BH * N * D * 2);
-  const Range rwq = span(q_norm_w, D * 4), rwk = span(k_norm_w, D * 4), rp = span(pos_ids, N * 12);
-  Range rsq = none, rsk = none, rsv = none, rskw = none;
+  const int64_t S = streams.count;
+  const Plain plains[] = {{q_norm_w, S * D * 4}, {k_norm_w, S * D * 4}, {pos_ids, N * 12}, {q_scale, BH * 4},
+                          {k_scale, BH * 4},     {v_scale, BH * 4},     {k_scale_work, BH * 4}};
+  // k_work: exactly k (in place) or apart from everything else
+  if (!same_view(kw, k) && !disjoint(kw, k, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+  if (!disjoint(kw, q, B, H, N, D, E) || !disjoint(kw, v, B, H, N, D, E)) return FLUXATTN_ERR_ALIASING;
+  if (overlap(extent(kw, B, H, N, D, E), extent(o, B, H, N, D, 2)) || !apart(kw, B, H, N, D, E, plains, 7))
+    return FLUXATTN_ERR_ALIASING;
+  // o: apart from every input and k_work
+  for (const View *w : {&q, &k, &v})
+    if (overlap(extent(o, B, H, N, D, 2), extent(*w, B, H, N, D, E))) return FLUXATTN_ERR_ALIASING;
+  if (!apart(o, B, H, N, D, 2, plains, 7)) return FLUXATTN_ERR_ALIASING;
   if (FP8) {
-    rsq = span(q_scale, BH * 4);
-    rsk = span(k_scale, BH * 4);
-    rsv = span(v_scale, BH * 4);
-    rskw = span(k_scale_work, BH * 4);
-  }
-  {
-    // k_work: exactly k (in place) or apart from everything else
-    const Range kw_others[] = {rq, rv, ro, rwq, rwk, rp, rsq, rsk, rsv, rskw};
-    if (!output_ok(rkw, rk, kw_others, 10)) return FLUXATTN_ERR_ALIASING;
-    const Range o_others[] = {rq, rk, rv, rkw, rwq, rwk, rp, rsq, rsk, rsv, rskw};
-    if (!output_ok(ro, none, o_others, 11)) return FLUXATTN_ERR_ALIASING;
-    if (FP8) {
-      const Range s_others[] = {rq, rk, rv, rkw, ro, rwq, rwk, rp, rsq, rsk, rsv};
-      if (!output_ok(rskw, none, s_others, 11)) return FLUXATTN_ERR_ALIASING;
-    }
+    // the new key scales: apart from all other buffers
+    const Range r = span(k_scale_work, BH * 4);
+    for (const View *w : {&q, &k, &v, &kw})
+      if (overlap(r, extent(*w, B, H, N, D, E))) return FLUXATTN_ERR_ALIASING;
+    if (overlap(r, extent(o, B, H, N, D, 2))) return FLUXATTN_ERR_ALIASING;
+    for (int i = 0; i < 6; ++i)
+      if (overlap(r, span(plains[i].p, plains[i].bytes))) return FLUXATTN_ERR_ALIASING;
   }
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
-  // both calls below re-validate a subset of the above and cannot fail it
-  fluxattn_status s = prologue_impl<FP8>(nullptr, k, nullptr, k_scale, nullptr, k_work, nullptr, k_scale_work,
-                                         nullptr, k_norm_w, pos_ids, B, H, N, D, at, ah, aw, theta, eps, stream);
+  // both calls re-validate a subset of the above and cannot fail it
+  fluxattn_status s = prologue_core<FP8>(View{}, k, nullptr, k_scale, View{}, kw, nullptr, k_scale_work, nullptr,
+                                         k_norm_w, streams, pos_ids, B, H, N, D, at, ah, aw, theta, eps, stream);
   if (s != FLUXATTN_OK) return s;
-  return fused_impl<FP8>(q, k_work, v, q_scale, k_scale_work, v_scale, o, q_norm_w, pos_ids, B, H, N, D, at, ah,
-                         aw, theta, eps, softmax_scale, stream);
+  return forward_core<FP8>(q, kw, v, q_scale, k_scale_work, v_scale, o, B, H, N, D, softmax_scale, true, q_norm_w,
+                           streams, pos_ids, at, ah, aw, theta, eps, stream);
 }
+
+const fluxattn_streams kOneStream = {1, {0, 0, 0, 0}};
 
 }  // namespace
 
@@ -328,8 +429,9 @@ fluxattn_status fluxattn_qk_norm_rope_bf16(const void *q, const void *k, void *q
                                            const int32_t *pos_ids, int64_t B, int64_t H, int64_t N,
                                            int64_t D, int32_t axes_t, int32_t axes_h, int32_t axes_w,
                                            float theta, float eps, void *stream) {
-  return prologue_impl<false>(q, k, nullptr, nullptr, q_out, k_out, nullptr, nullptr, q_norm_w, k_norm_w,
-                              pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, stream);
+  return prologue_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), nullptr, nullptr,
+                              contiguous(q_out, H, N, D), contiguous(k_out, H, N, D), nullptr, nullptr, q_norm_w,
+                              k_norm_w, kOneStream, pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, stream);
 }
 
 fluxattn_status fluxattn_qk_norm_rope_fp8(const uint8_t *q, const uint8_t *k, const float *q_scale,
@@ -338,20 +440,71 @@ fluxattn_status fluxattn_qk_norm_rope_fp8(const uint8_t *q, const uint8_t *k, co
                                           const float *k_norm_w, const int32_t *pos_ids, int64_t B,
                                           int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
                                           int32_t axes_w, float theta, float eps, void *stream) {
-  return prologue_impl<true>(q, k, q_scale, k_scale, q_out, k_out, q_scale_out, k_scale_out, q_norm_w,
-                             k_norm_w, pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, stream);
+  return prologue_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), q_scale, k_scale,
+                             contiguous(q_out, H, N, D), contiguous(k_out, H, N, D), q_scale_out, k_scale_out,
+                             q_norm_w, k_norm_w, kOneStream, pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta,
+                             eps, stream);
+}
+
+fluxattn_status fluxattn_qk_norm_rope_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                              fluxattn_layout k_layout, void *q_out, fluxattn_layout q_out_layout,
+                                              void *k_out, fluxattn_layout k_out_layout, const float *q_norm_w,
+                                              const float *k_norm_w, fluxattn_streams streams,
+                                              const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
+                                              int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta,
+                                              float eps, void *stream) {
+  return prologue_core<false>(view_of(q, q_layout), view_of(k, k_layout), nullptr, nullptr,
+                              view_of(q_out, q_out_layout), view_of(k_out, k_out_layout), nullptr, nullptr, q_norm_w,
+                              k_norm_w, streams, pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, stream);
+}
+
+fluxattn_status fluxattn_qk_norm_rope_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+                                             fluxattn_layout k_layout, const float *q_scale, const float *k_scale,
+                                             uint8_t *q_out, fluxattn_layout q_out_layout, uint8_t *k_out,
+                                             fluxattn_layout k_out_layout, float *q_scale_out, float *k_scale_out,
+                                             const float *q_norm_w, const float *k_norm_w,
+                                             fluxattn_streams streams, const int32_t *pos_ids, int64_t B,
+                                             int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
+                                             int32_t axes_w, float theta, float eps, void *stream) {
+  return prologue_core<true>(view_of(q, q_layout), view_of(k, k_layout), q_scale, k_scale,
+                             view_of(q_out, q_out_layout), view_of(k_out, k_out_layout), q_scale_out, k_scale_out,
+                             q_norm_w, k_norm_w, streams, pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps,
+                             stream);
 }
 
 fluxattn_status fluxattn_forward_bf16(const void *q, const void *k, const void *v, void *o, int64_t B,
                                       int64_t H, int64_t N, int64_t D, float softmax_scale, void *stream) {
-  return forward_impl<false>(q, k, v, nullptr, nullptr, nullptr, o, B, H, N, D, softmax_scale, stream);
+  return forward_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr,
+                             nullptr, nullptr, contiguous(o, H, N, D), B, H, N, D, softmax_scale, false, nullptr,
+                             kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, stream);
 }
 
 fluxattn_status fluxattn_forward_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
                                      const float *q_scale, const float *k_scale, const float *v_scale,
                                      void *o, int64_t B, int64_t H, int64_t N, int64_t D,
                                      float softmax_scale, void *stream) {
-  return forward_impl<true>(q, k, v, q_scale, k_scale, v_scale, o, B, H, N, D, softmax_scale, stream);
+  return forward_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale,
+                            k_scale, v_scale, contiguous(o, H, N, D), B, H, N, D, softmax_scale, false, nullptr,
+                            kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, stream);
+}
+
+fluxattn_status fluxattn_forward_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                         fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+                                         void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
+                                         int64_t D, float softmax_scale, void *stream) {
+  return forward_core<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
+                             nullptr, view_of(o, o_layout), B, H, N, D, softmax_scale, false, nullptr, kOneStream,
+                             nullptr, 0, 0, 0, 0.f, 0.f, stream);
+}
+
+fluxattn_status fluxattn_forward_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+                                        fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+                                        const float *q_scale, const float *k_scale, const float *v_scale, void *o,
+                                        fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N, int64_t D,
+                                        float softmax_scale, void *stream) {
+  return forward_core<true>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), q_scale, k_scale,
+                            v_scale, view_of(o, o_layout), B, H, N, D, softmax_scale, false, nullptr, kOneStream,
+                            nullptr, 0, 0, 0, 0.f, 0.f, stream);
 }
 
 fluxattn_status fluxattn_forward_fused_bf16(const void *q, const void *k, const void *v, void *o,
@@ -359,8 +512,9 @@ fluxattn_status fluxattn_forward_fused_bf16(const void *q, const void *k, const 
                                             int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
                                             int32_t axes_w, float theta, float eps, float softmax_scale,
                                             void *stream) {
-  return fused_impl<false>(q, k, v, nullptr, nullptr, nullptr, o, q_norm_w, pos_ids, B, H, N, D, axes_t, axes_h,
-                           axes_w, theta, eps, softmax_scale, stream);
+  return forward_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr,
+                             nullptr, nullptr, contiguous(o, H, N, D), B, H, N, D, softmax_scale, true, q_norm_w,
+                             kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, stream);
 }
 
 fluxattn_status fluxattn_forward_fused_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -369,8 +523,9 @@ fluxattn_status fluxattn_forward_fused_fp8(const uint8_t *q, const uint8_t *k, c
                                            int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
                                            int32_t axes_w, float theta, float eps, float softmax_scale,
                                            void *stream) {
-  return fused_impl<true>(q, k, v, q_scale, k_scale, v_scale, o, q_norm_w, pos_ids, B, H, N, D, axes_t, axes_h,
-                          axes_w, theta, eps, softmax_scale, stream);
+  return forward_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale,
+                            k_scale, v_scale, contiguous(o, H, N, D), B, H, N, D, softmax_scale, true, q_norm_w,
+                            kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, stream);
 }
 
 fluxattn_status fluxattn_joint_attention_bf16(const void *q, const void *k, const void *v, void *k_work,
@@ -378,7 +533,8 @@ fluxattn_status fluxattn_joint_attention_bf16(const void *q, const void *k, cons
                                               const int32_t *pos_ids, int64_t B, int64_t H, int64_t N,
                                               int64_t D, int32_t axes_t, int32_t axes_h, int32_t axes_w,
                                               float theta, float eps, float softmax_scale, void *stream) {
-  return joint_impl<false>(q, k, v, nullptr, nullptr, nullptr, k_work, nullptr, o, q_norm_w, k_norm_w, pos_ids,
+  return joint_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr, nullptr,
+                           nullptr, k_work, nullptr, contiguous(o, H, N, D), q_norm_w, k_norm_w, kOneStream, pos_ids,
                            B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
 }
 
@@ -389,8 +545,36 @@ fluxattn_status fluxattn_joint_attention_fp8(const uint8_t *q, const uint8_t *k,
                                              const int32_t *pos_ids, int64_t B, int64_t H, int64_t N,
                                              int64_t D, int32_t axes_t, int32_t axes_h, int32_t axes_w,
                                              float theta, float eps, float softmax_scale, void *stream) {
-  return joint_impl<true>(q, k, v, q_scale, k_scale, v_scale, k_work, k_scale_work, o, q_norm_w, k_norm_w,
+  return joint_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale, k_scale,
+                          v_scale, k_work, k_scale_work, contiguous(o, H, N, D), q_norm_w, k_norm_w, kOneStream,
                           pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+}
+
+fluxattn_status fluxattn_joint_attention_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                                 fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+                                                 void *k_work, void *o, fluxattn_layout o_layout,
+                                                 const float *q_norm_w, const float *k_norm_w,
+                                                 fluxattn_streams streams, const int32_t *pos_ids, int64_t B,
+                                                 int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
+                                                 int32_t axes_w, float theta, float eps, float softmax_scale,
+                                                 void *stream) {
+  return joint_core<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
+                           nullptr, k_work, nullptr, view_of(o, o_layout), q_norm_w, k_norm_w, streams, pos_ids, B, H,
+                           N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+}
+
+fluxattn_status fluxattn_joint_attention_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+                                                fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+                                                const float *q_scale, const float *k_scale, const float *v_scale,
+                                                uint8_t *k_work, float *k_scale_work, void *o,
+                                                fluxattn_layout o_layout, const float *q_norm_w,
+                                                const float *k_norm_w, fluxattn_streams streams,
+                                                const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
+                                                int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta,
+                                                float eps, float softmax_scale, void *stream) {
+  return joint_core<true>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), q_scale, k_scale,
+                          v_scale, k_work, k_scale_work, view_of(o, o_layout), q_norm_w, k_norm_w, streams, pos_ids,
+                          B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
 }
 
 const char *fluxattn_status_string(fluxattn_status s) {
@@ -408,6 +592,6 @@ const char *fluxattn_status_string(fluxattn_status s) {
 
 int fluxattn_last_hip_error(void) { return g_last_hip_error; }
 
-int fluxattn_version(void) { return 110; }
+int fluxattn_version(void) { return 120; }
 
 }  // extern "C"

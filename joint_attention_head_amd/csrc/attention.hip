@@ -149,17 +149,19 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
 // 64 dims this lane holds: 16 kk + 8 hi + i; the other 64 are in lane ^ 32).
 template <bool FP8>
 __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const char *qbase,
-                                             uint32_t head_bytes, int q_row, int hi, float q_scale) {
+                                             uint32_t head_bytes, uint32_t row_bytes, int q_row, int hi,
+                                             float q_scale) {
+  constexpr int kElem = FP8 ? 1 : 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
   // raw codes / values stay packed until the transform
   u32x2_t raw8[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const uint32_t elem = (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi;
+    const uint32_t off = (uint32_t)q_row * row_bytes + (uint32_t)((16 * kk + 8 * hi) * kElem);
     if constexpr (FP8) {
-      raw8[kk] = __builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0);
+      raw8[kk] = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
     } else {
-      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
+      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
   }
   auto values = [&](int kk, float (&x)[8]) __attribute__((always_inline)) {
@@ -195,12 +197,15 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
   // row serves, their outputs are never stored)
   const int tok = min(q_row, a.N - 1);
   const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
+  // norm weights of this token's stream
+  const int sid = (tok >= a.streams.start[1]) + (tok >= a.streams.start[2]) + (tok >= a.streams.start[3]);
+  const float *w_q = a.w_q + sid * kHeadDim;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     float x[8];
     values(kk, x);
-    const float4 w0 = *reinterpret_cast<const float4 *>(a.w_q + 16 * kk + 8 * hi);
-    const float4 w1 = *reinterpret_cast<const float4 *>(a.w_q + 16 * kk + 8 * hi + 4);
+    const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi);
+    const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi + 4);
     const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -223,7 +228,7 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
   }
 }
 
-template <bool FP8, bool FUSEQ>
+template <bool FP8, bool FUSEQ, bool STRIDED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int simd_of_wave[kWaves];
@@ -258,12 +263,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const int qt = logical - bh * ntiles;
 
   constexpr int kElem = FP8 ? 1 : 2;
-  constexpr uint32_t kTileGlobal = kBC * kHeadDim * kElem;   // bytes of one K/V tile in HBM
-  const size_t head_elems = (size_t)N * kHeadDim;
-  const uint32_t head_bytes = (uint32_t)(head_elems * kElem);
-  const char *qbase = static_cast<const char *>(a.q) + (size_t)bh * head_elems * kElem;
-  const char *kbase = static_cast<const char *>(a.k) + (size_t)bh * head_elems * kElem;
-  const char *vbase = static_cast<const char *>(a.v) + (size_t)bh * head_elems * kElem;
+  // ---- per-head base pointers, token-row pitches and buffer extents.
+  // Contiguous [B, H, N, D]: rows of 128 elements.  Strided views: the
+  // caller's (b, h, n) element strides; a head's extent ends with its last
+  // row, so rows past N read as zero.
+  struct View {
+    const char *base;
+    uint32_t row;     // bytes per token row
+    uint32_t bytes;   // buffer extent of the head
+  };
+  auto view = [&](const void *p, const Strides &st, int esize) __attribute__((always_inline)) {
+    View v;
+    if constexpr (STRIDED) {
+      const int64_t b = bh / a.H, h = bh - b * a.H;
+      v.base = static_cast<const char *>(p) + (b * st.b + h * st.h) * esize;
+      v.row = (uint32_t)st.n * (uint32_t)esize;
+      v.bytes = (uint32_t)(N - 1) * v.row + (uint32_t)(kHeadDim * esize);
+    } else {
+      v.base = static_cast<const char *>(p) + (size_t)bh * N * kHeadDim * esize;
+      v.row = (uint32_t)(kHeadDim * esize);
+      v.bytes = (uint32_t)N * v.row;
+    }
+    return v;
+  };
+  const View vq = view(a.q, a.sq, kElem), vk = view(a.k, a.sk, kElem), vv = view(a.v, a.sv, kElem);
+  const View vo = view(a.o, a.so, 2);
+  const char *qbase = vq.base;
+  const char *kbase = vk.base;
+  const char *vbase = vv.base;
 
   float c = a.scale_log2;
   float o_scale = 1.f;
@@ -277,11 +304,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // ---- per-tile buffer descriptors: base moved to the tile, records cut
   // to what is left of the head, so lane offsets stay tile-independent and
   // reads past the head's end still return zero.  Scalar arithmetic only.
-  auto tile_rsrc = [&](const char *base, int t) __attribute__((always_inline)) {
-    return make_rsrc(base + (size_t)t * kTileGlobal, head_bytes - (uint32_t)t * kTileGlobal);
+  auto tile_rsrc = [&](const View &v, int t) __attribute__((always_inline)) {
+    const uint32_t skip = (uint32_t)t * (uint32_t)kBC * v.row;
+    return make_rsrc(v.base + skip, v.bytes - skip);
   };
-  auto tile_words = [&](const char *base, int t) __attribute__((always_inline)) {
-    return rsrc_words(base + (size_t)t * kTileGlobal, head_bytes - (uint32_t)t * kTileGlobal);
+  auto tile_words = [&](const View &v, int t) __attribute__((always_inline)) {
+    const uint32_t skip = (uint32_t)t * (uint32_t)kBC * v.row;
+    return rsrc_words(v.base + skip, v.bytes - skip);
   };
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
@@ -290,7 +319,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   //     dims 4 dq .. +3 (dq = rank / 8): load i reads key 32 g + 4 kg + i,
   //     and the transposed 4x4 block goes to V^T rows 4 dq + jj.
   const int kg = rank & 7, dq = rank >> 3;
-  const uint32_t v_goff = (uint32_t)((32 * group + 4 * kg) * kHeadDim + 4 * dq) * kElem;
+  // offset of load i: v_goff + i * vv.row (an immediate for contiguous
+  // tensors; separate registers for strided ones)
+  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq * kElem);
+  uint32_t v_goffs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v_goffs[i] = v_goff + (uint32_t)i * vv.row;
   // (rows 4 dq + 1 and 4 dq + 3 share the swizzle of rows 4 dq and 4 dq + 2
   // and sit 128 bytes after them)
   uint32_t v_soff[2];
@@ -302,7 +336,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   }
   //  fp8 K: chunks rank and rank + 256 of the group's 512 16-byte chunks
   //     (8 keys per lane-load), widened to bf16 on the way to LDS.
-  const uint32_t k_goff = (uint32_t)((32 * group + (rank >> 4)) * kHeadDim + 8 * (rank & 15)) * kElem;
+  const uint32_t k_goff = (uint32_t)(32 * group + (rank >> 4)) * vk.row + (uint32_t)(8 * (rank & 15) * kElem);
+  const uint32_t k_goffs[2] = {k_goff, k_goff + 16u * vk.row};
   // (chunk rank + 256 is 16 keys further: same swizzle, 4 KiB on)
   const uint32_t k_soff = (uint32_t)k_off(32 * group + (rank >> 4), rank & 15);
   //  bf16 K by direct copies: wave gw of group g copies rows
@@ -314,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int row = 32 * group + 8 * gw + 4 * i + (lane >> 4);
     const int ch = (lane & 15) ^ (row & 15);
-    k_dgoff[i] = (uint32_t)(row * kHeadDim + 8 * ch) * 2;
+    k_dgoff[i] = (uint32_t)row * vk.row + (uint32_t)(8 * ch * 2);
   }
   const uint32_t k_m0 = lds_base + 256u * (uint32_t)(32 * group + 8 * gw);
   //  MFMA fragments: K (kk) row l32, chunk 2 kk + hi; V^T (st) row l32,
@@ -332,14 +367,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   u32x2_t vt_data[4];     // transposed V rows, ready for LDS
   u32x4_t kt_data[2];     // fp8 K widened to bf16, ready for LDS
   auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
+    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim * kElem);
     if constexpr (FP8) {
-      vraw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(r, v_goff + (uint32_t)(i * kHeadDim * kElem), 0, 0);
+      vraw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     } else {
-      vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, v_goff + (uint32_t)(i * kHeadDim * kElem), 0, 0);
+      vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     }
   };
   auto fetch_k_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
-    kraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, k_goff + (uint32_t)(16 * i * kHeadDim * kElem), 0, 0);
+    const uint32_t off = STRIDED ? k_goffs[i] : k_goff + (uint32_t)(16 * i * kHeadDim * kElem);
+    kraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   };
   // VGPR -> transposed rows (vector half-step work)
   auto prepare_v = [&]() __attribute__((always_inline)) {
@@ -382,13 +419,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1 (fp8) or
   // 0, 1, 2 (bf16 copies) in LDS; V tile 2 and fp8 K tile 2 in registers.
   for (int j = 0; j < 2 && j < T; ++j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, j);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
     prepare_v();
     store_v(j * kVTileBytes);
     if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, j);
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(vk, j);
 #pragma unroll
       for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
       prepare_k();
@@ -397,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   }
   if constexpr (!FP8) {
     for (int j = 0; j < 3 && j < T; ++j) {
-      const i32x4_t w = tile_words(kbase, j);
+      const i32x4_t w = tile_words(vk, j);
       k_dma_one(w, j * kKTileBytes, 0);
       k_dma_one(w, j * kKTileBytes, 1);
     }
@@ -405,11 +442,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   }
   {
     const int t2 = min(2, T - 1);
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, t2);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, t2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
     if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, t2);
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(vk, t2);
 #pragma unroll
       for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
     }
@@ -420,16 +457,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
   if constexpr (FUSEQ) {
-    load_q_fused<FP8>(qf, a, qbase, head_bytes, q_row, hi, FP8 ? a.q_scale[bh] : 1.f);
+    load_q_fused<FP8>(qf, a, qbase, vq.bytes, vq.row, q_row, hi, FP8 ? a.q_scale[bh] : 1.f);
   } else {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, vq.bytes);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t elem = (uint32_t)q_row * kHeadDim + 16 * kk + 8 * hi;
+      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * kElem);
       if constexpr (FP8) {
-        qf[kk] = __builtin_bit_cast(bf16x8_t, e4m3x8_to_bf16x8(__builtin_amdgcn_raw_buffer_load_b64(rq, elem, 0, 0)));
+        qf[kk] = __builtin_bit_cast(bf16x8_t, e4m3x8_to_bf16x8(__builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0)));
       } else {
-        qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, elem * 2, 0, 0));
+        qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
       }
     }
   }
@@ -597,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // slots of tile j+2
     constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
     const int tn = min(j + 3, T - 1);
-    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vbase, tn);
+    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn);
     // the vector half-step wrote no LDS, and the fragment reads it issued
     // touch a slot no wave writes before the next barrier: a plain barrier
     // that does not wait for them
@@ -623,9 +660,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) {
         const int i = step == kKLoad0 ? 0 : 1;
         if constexpr (FP8) {
-          fetch_k_one(tile_rsrc(kbase, tn), i);
+          fetch_k_one(tile_rsrc(vk, tn), i);
         } else {
-          k_dma_one(tile_words(kbase, tn), kPlus3, i);
+          k_dma_one(tile_words(vk, tn), kPlus3, i);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -668,8 +705,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
   }
   const float inv = o_scale / l_run;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(a.o) + (size_t)bh * head_elems * 2,
-                                              (uint32_t)(head_elems * 2));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -677,12 +713,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       u32x2_t w;
       w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
       w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-      const uint32_t elem = (uint32_t)q_row * kHeadDim + 32 * db + 8 * g + 4 * hi;
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, elem * 2, 0, 0);
+      const uint32_t off = (uint32_t)q_row * vo.row + (uint32_t)((32 * db + 8 * g + 4 * hi) * 2);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
     }
 }
 
-template <bool FP8, bool FUSEQ>
+template <bool FP8, bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.N + kBR - 1) / kBR;
   const int64_t grid = ntiles * a.BH;
@@ -694,21 +730,30 @@ hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FP8, FUSEQ>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FP8, FUSEQ, STRIDED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8, FUSEQ>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<FP8, FUSEQ, STRIDED>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s) { return launch<false, false>(a, s); }
-hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s) { return launch<true, false>(a, s); }
-hipError_t launch_forward_fused_bf16(const ForwardArgs &a, hipStream_t s) { return launch<false, true>(a, s); }
-hipError_t launch_forward_fused_fp8(const ForwardArgs &a, hipStream_t s) { return launch<true, true>(a, s); }
+hipError_t launch_forward(const ForwardArgs &a, bool fp8, bool fused, bool strided, hipStream_t s) {
+  const int v = (fp8 ? 4 : 0) | (fused ? 2 : 0) | (strided ? 1 : 0);
+  switch (v) {
+    case 0: return launch<false, false, false>(a, s);
+    case 1: return launch<false, false, true>(a, s);
+    case 2: return launch<false, true, false>(a, s);
+    case 3: return launch<false, true, true>(a, s);
+    case 4: return launch<true, false, false>(a, s);
+    case 5: return launch<true, false, true>(a, s);
+    case 6: return launch<true, true, false>(a, s);
+    default: return launch<true, true, true>(a, s);
+  }
+}
 
 int64_t forward_grid_blocks(int64_t BH, int64_t N) { return BH * ((N + kBR - 1) / kBR); }
 

@@ -16,16 +16,32 @@ struct RopeTable {
   int8_t axis[kPairs];
 };
 
+// Element strides of a [B, H, N, D] view (D contiguous).
+struct Strides {
+  int64_t b, h;
+  int32_t n;
+};
+
+// Token ranges with their own norm weights: stream s covers tokens
+// [start[s], start[s+1]); unused entries hold INT32_MAX.
+struct Streams {
+  int32_t start[4];   // start[0] = 0
+};
+
 struct PrologueArgs {
   const void *q, *k;
   void *q_out, *k_out;
-  const float *w_q, *w_k;
+  const float *w_q, *w_k;             // [streams, D]
   const int32_t *pos;
   const float *q_scale, *k_scale;     // fp8 only
   float *q_scale_out, *k_scale_out;   // fp8 only
   int64_t BH;                         // B * H
+  int32_t H;
   int32_t N;
   float eps;
+  Strides sq, sk, sqo, sko;
+  Streams streams;
+  int32_t num_streams;
 };
 
 struct ForwardArgs {
@@ -33,8 +49,11 @@ struct ForwardArgs {
   void *o;
   const float *q_scale, *k_scale, *v_scale;  // fp8 only
   int32_t BH;
+  int32_t H;
   int32_t N;
   float scale_log2;   // softmax_scale * log2(e)
+  Strides sq, sk, sv, so;   // used by the strided kernels only
+  Streams streams;          // fused query prologue only
   // fused query prologue only: raw q is normalised and rotated on load.
   // Pair p of axis a (pairs rope_first[a] .. rope_first[a+1]-1) turns by
   // pos[a] * 2^((p - rope_first[a]) * rope_log2_step[a]), with
@@ -50,11 +69,10 @@ hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
                                 hipStream_t s);
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
                                hipStream_t s);
-hipError_t launch_forward_bf16(const ForwardArgs &a, hipStream_t s);
-hipError_t launch_forward_fp8(const ForwardArgs &a, hipStream_t s);
-// attention whose Q load applies RMSNorm + RoPE to raw queries
-hipError_t launch_forward_fused_bf16(const ForwardArgs &a, hipStream_t s);
-hipError_t launch_forward_fused_fp8(const ForwardArgs &a, hipStream_t s);
+// Attention launches.  fused: the Q load applies RMSNorm + RoPE to raw
+// queries.  strided: q, k, v, o follow the strides in the arguments (else
+// contiguous [B, H, N, D]).
+hipError_t launch_forward(const ForwardArgs &a, bool fp8, bool fused, bool strided, hipStream_t s);
 
 // Workgroups the forward kernel launches for B*H heads of N tokens.
 int64_t forward_grid_blocks(int64_t BH, int64_t N);

@@ -76,6 +76,29 @@ __device__ __forceinline__ void norm_rope8(float (&f)[8], const float (&w)[8],
   }
 }
 
+// Walks the heads bh = 0, 1, 2, ... (b = bh / H, h = bh % H) of an input
+// and an output view, keeping each head's element offset b*st.b + h*st.h
+// without a division.  Every value is uniform over the workgroup.
+struct HeadWalk {
+  int64_t in, out;   // offsets of the current head in the two views
+  int32_t h;
+  __device__ __forceinline__ void next(const Strides &si, const Strides &so, int32_t H) {
+    if (++h == H) {
+      h = 0;
+      in += si.b - (int64_t)(H - 1) * si.h;
+      out += so.b - (int64_t)(H - 1) * so.h;
+    } else {
+      in += si.h;
+      out += so.h;
+    }
+  }
+};
+
+// Stream (norm-weight set) of a token.
+__device__ __forceinline__ int stream_of(const Streams &ss, int tok) {
+  return (tok >= ss.start[1]) + (tok >= ss.start[2]) + (tok >= ss.start[3]);
+}
+
 __device__ __forceinline__ void lane_angles(const PrologueArgs &a, const RopeTable &t,
                                             int tok, int c, float (&cs)[4], float (&sn)[4]) {
   const int32_t p0 = a.pos[3 * (int64_t)tok + 0];
@@ -99,22 +122,31 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
   float cs[4], sn[4];
   lane_angles(a, t, tok, c, cs, sn);
 
+  const int sid = stream_of(a.streams, tok);
   for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint16_t *src = static_cast<const uint16_t *>(which ? a.k : a.q);
     uint16_t *dst = static_cast<uint16_t *>(which ? a.k_out : a.q_out);
-    const float *wp = which ? a.w_k : a.w_q;
+    const Strides &si = which ? a.sk : a.sq;
+    const Strides &so = which ? a.sko : a.sqo;
+    const float *wp = (which ? a.w_k : a.w_q) + sid * kHeadDim;
     float w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
 
-    const int64_t row_stride = (int64_t)a.N * kHeadDim;
-    const int64_t base = (int64_t)tok * kHeadDim + 8 * c;
+    const int64_t tin = (int64_t)tok * si.n + 8 * c, tout = (int64_t)tok * so.n + 8 * c;
+    HeadWalk walk{0, 0, 0};
     for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+      int64_t oin[kUnroll], oout[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        oin[u] = walk.in + tin;
+        oout[u] = walk.out + tout;
+        walk.next(si, so, a.H);
+      }
       uint4 x[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (bh0 + u < a.BH)
-          x[u] = *reinterpret_cast<const uint4 *>(src + (bh0 + u) * row_stride + base);
+        if (bh0 + u < a.BH) x[u] = *reinterpret_cast<const uint4 *>(src + oin[u]);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         if (bh0 + u >= a.BH) break;
@@ -126,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
         y.y = pack_bf16(f[2], f[3]);
         y.z = pack_bf16(f[4], f[5]);
         y.w = pack_bf16(f[6], f[7]);
-        *reinterpret_cast<uint4 *>(dst + (bh0 + u) * row_stride + base) = y;
+        *reinterpret_cast<uint4 *>(dst + oout[u]) = y;
       }
     }
   }
@@ -153,8 +185,13 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
   // Output scale sqrt(D) * max|w| / 448: every output lies within +-448 of it.
   float sq, sk;
   {
-    const float mq = a.w_q ? wave_max(fmaxf(fabsf(a.w_q[lane]), fabsf(a.w_q[lane + 64]))) : 0.f;
-    const float mk = wave_max(fmaxf(fabsf(a.w_k[lane]), fabsf(a.w_k[lane + 64])));
+    float mq = 0.f, mk = 0.f;
+    for (int st = 0; st < a.num_streams; ++st) {
+      if (a.w_q) mq = fmaxf(mq, fmaxf(fabsf(a.w_q[st * kHeadDim + lane]), fabsf(a.w_q[st * kHeadDim + lane + 64])));
+      mk = fmaxf(mk, fmaxf(fabsf(a.w_k[st * kHeadDim + lane]), fabsf(a.w_k[st * kHeadDim + lane + 64])));
+    }
+    mq = wave_max(mq);
+    mk = wave_max(mk);
     const float root_d = 11.313708498984760f;  // sqrt(128)
     sq = mq > 0.f ? root_d * mq / 448.f : 1.f;
     sk = mk > 0.f ? root_d * mk / 448.f : 1.f;
@@ -172,25 +209,35 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
   float cs[4], sn[4];
   lane_angles(a, t, tok, c, cs, sn);
 
+  const int sid = stream_of(a.streams, tok);
   for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint8_t *src = static_cast<const uint8_t *>(which ? a.k : a.q);
     uint8_t *dst = static_cast<uint8_t *>(which ? a.k_out : a.q_out);
-    const float *wp = which ? a.w_k : a.w_q;
+    const Strides &si = which ? a.sk : a.sq;
+    const Strides &so = which ? a.sko : a.sqo;
+    const float *wp = (which ? a.w_k : a.w_q) + sid * kHeadDim;
     const float *s_in = which ? a.k_scale : a.q_scale;
     const float inv_out = 1.0f / (which ? sk : sq);
     float w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
 
-    const int64_t row_stride = (int64_t)a.N * kHeadDim;
-    const int64_t base = (int64_t)tok * kHeadDim + 8 * c;
+    const int64_t tin = (int64_t)tok * si.n + 8 * c, tout = (int64_t)tok * so.n + 8 * c;
+    HeadWalk walk{0, 0, 0};
     for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+      int64_t oin[kUnroll], oout[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        oin[u] = walk.in + tin;
+        oout[u] = walk.out + tout;
+        walk.next(si, so, a.H);
+      }
       uint2 x[kUnroll];
       float s[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
         if (bh0 + u < a.BH) {
-          x[u] = *reinterpret_cast<const uint2 *>(src + (bh0 + u) * row_stride + base);
+          x[u] = *reinterpret_cast<const uint2 *>(src + oin[u]);
           s[u] = s_in[bh0 + u];
         }
 #pragma unroll
@@ -207,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
         uint2 y;
         y.x = f32x4_to_e4m3(f);
         y.y = f32x4_to_e4m3(f + 4);
-        *reinterpret_cast<uint2 *>(dst + (bh0 + u) * row_stride + base) = y;
+        *reinterpret_cast<uint2 *>(dst + oout[u]) = y;
       }
     }
   }

@@ -88,6 +88,26 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     return x * np.asarray(w, dtype=np.float64) / np.sqrt(ms + eps)
 
 
+def stream_weights(w_rows, starts, N: int) -> np.ndarray:
+    """Per-token RMSNorm weights [N, D] of a sequence made of token streams.
+
+    The joint sequence is the text stream, then the target-image stream, then
+    the optional reference-image stream; up to the joint attention each
+    stream has its own projection and normalisation weights (blog post
+    "Speed up image generation with FLUX 3 Image Klein on NVIDIA Blackwell
+    GPUs", section "Running FLUX 3 inference with TensorRT LLM VisualGen").
+    Stream s holds tokens [starts[s], starts[s+1]) (the last runs to N) and
+    uses row w_rows[s].  rms_norm broadcasts the result over batch and heads.
+    """
+    w_rows = np.asarray(w_rows, dtype=np.float64)
+    bounds = [int(x) for x in starts] + [N]
+    assert w_rows.shape[0] == len(starts) and bounds[0] == 0
+    out = np.empty((N, w_rows.shape[1]), dtype=np.float64)
+    for s in range(len(starts)):
+        out[bounds[s]:bounds[s + 1]] = w_rows[s]
+    return out
+
+
 # --------------------------------------------------------------------------
 # 3. three-axis rotary position embedding
 # --------------------------------------------------------------------------

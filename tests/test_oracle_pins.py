@@ -84,6 +84,40 @@ def test_rmsnorm_weight_is_per_dimension():
     np.testing.assert_allclose(y[37], 2 * x[37] / math.sqrt(np.mean(x * x) + EPS), rtol=1e-14)
 
 
+def test_stream_weights_brute_force_per_token():
+    """Each token takes the weight row of the last stream starting at or
+    before it; checked with plain loops, including empty streams."""
+    rng = np.random.default_rng(4)
+    D, N = 8, 11
+    x = rng.standard_normal((2, 3, N, D))
+    rows = 1 + 0.1 * rng.standard_normal((4, D))
+    for starts in ((0,), (0, 4), (0, 4, 9), (0, 0, 5), (0, 3, 3, 11), (0, 11)):
+        S = len(starts)
+        got = oracle.rms_norm(x, oracle.stream_weights(rows[:S], starts, N), EPS)
+        for b in range(2):
+            for h in range(3):
+                for n in range(N):
+                    s = 0
+                    for j in range(S):
+                        if starts[j] <= n:
+                            s = j
+                    ss = 0.0
+                    for d in range(D):
+                        ss += x[b, h, n, d] ** 2
+                    for d in range(D):
+                        want = x[b, h, n, d] * rows[s, d] / math.sqrt(ss / D + EPS)
+                        assert abs(got[b, h, n, d] - want) <= 1e-13 * max(1.0, abs(want))
+
+
+def test_stream_weights_one_stream_is_the_shared_vector():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 2, 7, 128))
+    w = 1 + 0.1 * rng.standard_normal(128)
+    tok = oracle.stream_weights(w[None], (0,), 7)
+    assert tok.shape == (7, 128) and np.array_equal(tok, np.broadcast_to(w, (7, 128)))
+    np.testing.assert_array_equal(oracle.rms_norm(x, tok, EPS), oracle.rms_norm(x, w, EPS))
+
+
 # ----------------------------------------------------------------- RoPE
 
 def _basis(d):

@@ -80,6 +80,24 @@ def position_ids(n_txt: int, grid, ref_grid=None) -> np.ndarray:
     return np.ascontiguousarray(np.concatenate(parts, axis=0))
 
 
+def stream_starts(w: Workload) -> tuple:
+    """First token of each stream in the joint sequence: text, target image
+    and, when present, reference image."""
+    starts = [0, w.n_txt]
+    if w.ref_grid is not None:
+        starts.append(w.n_txt + w.grid[0] * w.grid[1])
+    return tuple(starts)
+
+
+def stream_norm_weights(n_streams: int, seed: int = 0, D: int = HEAD_DIM):
+    """Per-stream fp32 norm weights [S, D] for queries and keys, each row
+    1 + 0.1*N(0,1) like the single-stream weights."""
+    g = torch.Generator(device="cpu").manual_seed(1000 + seed)
+    w_q = 1.0 + 0.1 * torch.randn(n_streams, D, generator=g, dtype=torch.float32)
+    w_k = 1.0 + 0.1 * torch.randn(n_streams, D, generator=g, dtype=torch.float32)
+    return w_q, w_k
+
+
 def randn_qkv(B: int, H: int, N: int, seed: int = 0, D: int = HEAD_DIM):
     """fp32 q, k, v ~ N(0,1) and norm weights 1 + 0.1*N(0,1), in recipe order."""
     g = torch.Generator(device="cpu").manual_seed(seed)
