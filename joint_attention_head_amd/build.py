@@ -18,7 +18,7 @@ LIB_NAME = "libfluxattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "prologue.hip", "attention.hip"]
+SOURCES = ["api.hip", "prologue.hip", "attention.hip", "attention_fp8.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -355,7 +355,8 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
   }
   const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
                          is_contiguous(o, H, N, D));
-  const hipError_t e = launch_forward(a, FP8, fused, strided, static_cast<hipStream_t>(stream));
+  const hipError_t e = FP8 ? launch_forward_fp8(a, fused, strided, static_cast<hipStream_t>(stream))
+                           : launch_forward_bf16(a, fused, strided, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
 }
 

@@ -34,10 +34,9 @@
 //    the vector half-step.
 //  * K tiles and V^T tiles of 64 keys go through two 4-slot LDS rings
 //    (64 KiB each).  Both groups load half of every tile, spread over their
-//    matrix half-steps: bf16 K by direct global -> LDS buffer loads, three
-//    tiles ahead; V (and fp8 K) global -> VGPR, permuted (widened) in the
-//    next vector half-step and written to LDS in the matrix half-step after
-//    that, two tiles ahead.  Buffer-resource loads return 0 past the end of a
+//    matrix half-steps: K by direct global -> LDS buffer loads, three tiles
+//    ahead; V global -> VGPR, permuted in the next vector half-step and
+//    written to LDS in the matrix half-step after that, two tiles ahead.  Buffer-resource loads return 0 past the end of a
 //    head, so ragged tails need no branches; the softmax masks keys >= N.
 //  * Online softmax in base 2: one FMA per score gives x = c*S - b (c =
 //    scale * log2 e, b = the row's running shift), then p = 2^x.  The row
@@ -49,10 +48,8 @@
 //  * blockIdx is remapped so that the workgroups the dispatcher sends to one
 //    XCD (blockIdx % 8) take consecutive query tiles of the same (b,h) and
 //    share its K/V stream through that XCD's L2.
-//  * fp8 (OCP E4M3) inputs are widened to bf16, which is exact; the
-//    per-(b,h) scales are folded into the softmax scale (q, k) and into the
-//    final normalisation (v).
-#include "fluxattn_internal.h"
+// FP8 inputs run on the fp8 matrix cores instead (attention_fp8.hip).
+#include "attn_common.h"
 
 #include <atomic>
 
@@ -68,64 +65,8 @@ constexpr int kKTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = key
 constexpr int kVTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = head dim
 constexpr int kVRingOffset = kSlots * kKTileBytes;
 constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 128 KiB
-constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw buffer, 32-bit data format
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-template <int R>
-struct Slot {
-  static constexpr int value = R;
-};
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2_t v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Four E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2_t r;
-  r[0] = pack_bf16(lo[0], lo[1]);
-  r[1] = pack_bf16(hi[0], hi[1]);
-  return r;
-}
-
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(u32x2_t w) {
-  const u32x2_t a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-  u32x4_t v;
-  v[0] = a[0];
-  v[1] = a[1];
-  v[2] = b[0];
-  v[3] = b[1];
-  return v;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
-// Raw buffer descriptor words (base, no stride, `bytes` records, 32-bit
-// data format); out-of-range offsets read as zero.
-__device__ __forceinline__ i32x4_t rsrc_words(const void *base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = (int)(uint32_t)p;
-  r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
-  r[2] = (int)bytes;
-  r[3] = (int)kRsrcWord3;
-  return r;
-}
+using namespace attn;
 
 // LDS layouts (K ring, then V^T ring; 16 KiB per slot).
 //  K tile : row = key (256 B), 16-byte chunk c of the head dim stored at
@@ -143,51 +84,26 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
-// Queries of the fused entry points: raw Q (fp8: times its scale) ->
-// RMSNorm over the 128 dims -> rotation of each adjacent pair by its
-// axis position times frequency -> bf16 (the prologue's operations, on the
-// 64 dims this lane holds: 16 kk + 8 hi + i; the other 64 are in lane ^ 32).
-template <bool FP8>
-__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const char *qbase,
-                                             uint32_t head_bytes, uint32_t row_bytes, int q_row, int hi,
-                                             float q_scale) {
-  constexpr int kElem = FP8 ? 1 : 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, head_bytes);
-  // raw codes / values stay packed until the transform
-  u32x2_t raw8[8];
+// Queries of the fused entry points: raw Q -> RMSNorm over the 128 dims ->
+// rotation of each adjacent pair by its axis position times frequency ->
+// bf16 (the prologue's operations, on the 64 dims this lane holds:
+// 16 kk + 8 hi + i; the other 64 are in lane ^ 32).
+__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const HeadView &vq, int q_row,
+                                             int hi) {
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const uint32_t off = (uint32_t)q_row * row_bytes + (uint32_t)((16 * kk + 8 * hi) * kElem);
-    if constexpr (FP8) {
-      raw8[kk] = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
-    } else {
-      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
+    const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
+    qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
   }
-  auto values = [&](int kk, float (&x)[8]) __attribute__((always_inline)) {
-    if constexpr (FP8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw8[kk][h], false);
-        const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw8[kk][h], true);
-        x[4 * h + 0] = lo[0] * q_scale;
-        x[4 * h + 1] = lo[1] * q_scale;
-        x[4 * h + 2] = up[0] * q_scale;
-        x[4 * h + 3] = up[1] * q_scale;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)qf[kk][i];
-    }
-  };
   float ss = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    float x[8];
-    values(kk, x);
+  for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-  }
+    for (int i = 0; i < 8; ++i) {
+      const float x = (float)qf[kk][i];
+      ss = fmaf(x, x, ss);
+    }
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
     ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
@@ -197,29 +113,19 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
   // row serves, their outputs are never stored)
   const int tok = min(q_row, a.N - 1);
   const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
-  // norm weights of this token's stream
-  const int sid = (tok >= a.streams.start[1]) + (tok >= a.streams.start[2]) + (tok >= a.streams.start[3]);
-  const float *w_q = a.w_q + sid * kHeadDim;
+  const float *w_q = stream_weights(a, tok);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     float x[8];
-    values(kk, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)qf[kk][i];
     const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi);
     const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi + 4);
     const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // pair pr = 8 kk + 4 hi + m: its axis, index inside the axis, angle
-      const int pr = 8 * kk + 4 * hi + m;
-      const int ax = pr < a.rope_first[1] ? 0 : (pr < a.rope_first[2] ? 1 : 2);
-      const int jj = pr - (ax == 0 ? 0 : (ax == 1 ? a.rope_first[1] : a.rope_first[2]));
-      const float step = ax == 0 ? a.rope_log2_step[0] : (ax == 1 ? a.rope_log2_step[1] : a.rope_log2_step[2]);
-      const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
-      // angle in revolutions, reduced to [0, 1) and fed to the hardware
-      // sin / cos: absolute error about 1e-6 + 4e-8 |angle| rad, the size
-      // of the fp32 rounding of the angle itself for FLUX's positions
-      const float rev = __builtin_amdgcn_fractf((float)p * exp2f((float)jj * step) * 0.15915494309189535f);
-      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      float sn, cs;
+      pair_rotation(a, pos, 8 * kk + 4 * hi + m, sn, cs);
       const float u = x[2 * m] * w[2 * m] * rstd;
       const float v = x[2 * m + 1] * w[2 * m + 1] * rstd;
       qf[kk][2 * m] = (__bf16)(u * cs - v * sn);
@@ -228,7 +134,7 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
   }
 }
 
-template <bool FP8, bool FUSEQ, bool STRIDED>
+template <bool FUSEQ, bool STRIDED>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int simd_of_wave[kWaves];
@@ -237,81 +143,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
 
-  // ---- ping-pong groups: sort waves by (SIMD, wave id); alternate groups
-  // along that order, so the two waves of a SIMD land in different groups.
-  if (lane == 0) simd_of_wave[wave] = (int)__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));
-  __syncthreads();
-  int order = 0;
-  {
-    const int mine = simd_of_wave[wave] * kWaves + wave;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) order += (simd_of_wave[w] * kWaves + w) < mine;
-  }
-  // the sort key is the same in every lane of a wave: keep it scalar
-  order = __builtin_amdgcn_readfirstlane(order);
+  // ---- ping-pong groups: the two waves of a SIMD land in different groups
+  const int order = pingpong_order(simd_of_wave, wave, lane);
   const int group = order & 1;
   const int gw = order >> 1;                   // wave index inside the group
   const int rank = gw * 64 + lane;             // 0..255 inside the group
 
   // ---- blockIdx -> (b*h, query tile), consecutive tiles per XCD
   const int ntiles = (N + kBR - 1) / kBR;
-  const int total = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
-  const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int bh = logical / ntiles;
   const int qt = logical - bh * ntiles;
 
-  constexpr int kElem = FP8 ? 1 : 2;
-  // ---- per-head base pointers, token-row pitches and buffer extents.
-  // Contiguous [B, H, N, D]: rows of 128 elements.  Strided views: the
-  // caller's (b, h, n) element strides; a head's extent ends with its last
-  // row, so rows past N read as zero.
-  struct View {
-    const char *base;
-    uint32_t row;     // bytes per token row
-    uint32_t bytes;   // buffer extent of the head
-  };
-  auto view = [&](const void *p, const Strides &st, int esize) __attribute__((always_inline)) {
-    View v;
-    if constexpr (STRIDED) {
-      const int64_t b = bh / a.H, h = bh - b * a.H;
-      v.base = static_cast<const char *>(p) + (b * st.b + h * st.h) * esize;
-      v.row = (uint32_t)st.n * (uint32_t)esize;
-      v.bytes = (uint32_t)(N - 1) * v.row + (uint32_t)(kHeadDim * esize);
-    } else {
-      v.base = static_cast<const char *>(p) + (size_t)bh * N * kHeadDim * esize;
-      v.row = (uint32_t)(kHeadDim * esize);
-      v.bytes = (uint32_t)N * v.row;
-    }
-    return v;
-  };
-  const View vq = view(a.q, a.sq, kElem), vk = view(a.k, a.sk, kElem), vv = view(a.v, a.sv, kElem);
-  const View vo = view(a.o, a.so, 2);
-  const char *qbase = vq.base;
-  const char *kbase = vk.base;
-  const char *vbase = vv.base;
+  // ---- per-head base pointers, token-row pitches and buffer extents
+  const HeadView vq = head_view<STRIDED>(a.q, a.sq, 2, bh, a.H, N);
+  const HeadView vk = head_view<STRIDED>(a.k, a.sk, 2, bh, a.H, N);
+  const HeadView vv = head_view<STRIDED>(a.v, a.sv, 2, bh, a.H, N);
+  const HeadView vo = head_view<STRIDED>(a.o, a.so, 2, bh, a.H, N);
 
-  float c = a.scale_log2;
-  float o_scale = 1.f;
-  if constexpr (FP8) {
-    c *= (FUSEQ ? 1.f : a.q_scale[bh]) * a.k_scale[bh];   // fused: Q arrives in true units
-    o_scale = a.v_scale[bh];
-  }
+  const float c = a.scale_log2;
   const int T = (N + kBC - 1) / kBC;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
-
-  // ---- per-tile buffer descriptors: base moved to the tile, records cut
-  // to what is left of the head, so lane offsets stay tile-independent and
-  // reads past the head's end still return zero.  Scalar arithmetic only.
-  auto tile_rsrc = [&](const View &v, int t) __attribute__((always_inline)) {
-    const uint32_t skip = (uint32_t)t * (uint32_t)kBC * v.row;
-    return make_rsrc(v.base + skip, v.bytes - skip);
-  };
-  auto tile_words = [&](const View &v, int t) __attribute__((always_inline)) {
-    const uint32_t skip = (uint32_t)t * (uint32_t)kBC * v.row;
-    return rsrc_words(v.base + skip, v.bytes - skip);
-  };
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
   // keys [32 g, 32 g + 32).
@@ -321,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const int kg = rank & 7, dq = rank >> 3;
   // offset of load i: v_goff + i * vv.row (an immediate for contiguous
   // tensors; separate registers for strided ones)
-  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq * kElem);
+  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq * 2);
   uint32_t v_goffs[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v_goffs[i] = v_goff + (uint32_t)i * vv.row;
@@ -334,13 +186,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) v_soff[h] = (uint32_t)(kVRingOffset + vt_off(4 * dq + 2 * h, ch) + within);
   }
-  //  fp8 K: chunks rank and rank + 256 of the group's 512 16-byte chunks
-  //     (8 keys per lane-load), widened to bf16 on the way to LDS.
-  const uint32_t k_goff = (uint32_t)(32 * group + (rank >> 4)) * vk.row + (uint32_t)(8 * (rank & 15) * kElem);
-  const uint32_t k_goffs[2] = {k_goff, k_goff + 16u * vk.row};
-  // (chunk rank + 256 is 16 keys further: same swizzle, 4 KiB on)
-  const uint32_t k_soff = (uint32_t)k_off(32 * group + (rank >> 4), rank & 15);
-  //  bf16 K by direct copies: wave gw of group g copies rows
+  //  K by direct copies: wave gw of group g copies rows
   //     32 g + 8 gw .. +8 with two buffer_load_dwordx4 ... lds; lane l of
   //     copy i fetches the chunk the K swizzle puts at LDS slot row
   //     32 g + 8 gw + 4 i + l / 16, chunk position l % 16.
@@ -362,27 +208,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   for (int st = 0; st < 4; ++st) vf[st] = (uint32_t)(kVRingOffset + vt_off(l32, 2 * st + hi));
 
   // ---- ring traffic helpers
-  u32x2_t vraw[4];        // bf16: 4 keys x 4 dims per lane; fp8: 4 keys x 4 dims in vraw[i][0]
-  u32x2_t kraw[2];        // fp8 K: 8 codes per chunk
+  u32x2_t vraw[4];        // 4 keys x 4 dims per lane
   u32x2_t vt_data[4];     // transposed V rows, ready for LDS
-  u32x4_t kt_data[2];     // fp8 K widened to bf16, ready for LDS
   auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
-    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim * kElem);
-    if constexpr (FP8) {
-      vraw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    } else {
-      vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    }
-  };
-  auto fetch_k_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
-    const uint32_t off = STRIDED ? k_goffs[i] : k_goff + (uint32_t)(16 * i * kHeadDim * kElem);
-    kraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim * 2);
+    vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   };
   // VGPR -> transposed rows (vector half-step work)
   auto prepare_v = [&]() __attribute__((always_inline)) {
     u32x2_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = FP8 ? e4m3x4_to_bf16x4(vraw[i][0]) : vraw[i];
+    for (int i = 0; i < 4; ++i) w[i] = vraw[i];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
@@ -391,20 +227,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       vt_data[jj][1] = __builtin_amdgcn_perm(w[3][h], w[2][h], sel);
     }
   };
-  auto prepare_k = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) kt_data[i] = e4m3x8_to_bf16x8(kraw[i]);
-  };
   auto store_v = [&](int slot_bytes) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
       *reinterpret_cast<u32x2_t *>(lds + v_soff[jj >> 1] + (slot_bytes + 128 * (jj & 1))) = vt_data[jj];
   };
-  auto store_k = [&](int slot_bytes) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t *>(lds + k_soff + (slot_bytes + 4096 * i)) = kt_data[i];
-  };
-  // one of the two direct K copies of this wave (bf16): 1 KiB = 4 rows
+  // one of the two direct K copies of this wave: 1 KiB = 4 rows
   auto k_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
     const uint32_t m0 = k_m0 + slot_bytes + 1024u * (uint32_t)i;
     asm volatile(
@@ -416,58 +244,38 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
         : "memory");
   };
 
-  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1 (fp8) or
-  // 0, 1, 2 (bf16 copies) in LDS; V tile 2 and fp8 K tile 2 in registers.
+  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1, 2 in
+  // LDS; V tile 2 in registers.
   for (int j = 0; j < 2 && j < T; ++j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j, kBC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
     prepare_v();
     store_v(j * kVTileBytes);
-    if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(vk, j);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
-      prepare_k();
-      store_k(j * kKTileBytes);
-    }
   }
-  if constexpr (!FP8) {
-    for (int j = 0; j < 3 && j < T; ++j) {
-      const i32x4_t w = tile_words(vk, j);
-      k_dma_one(w, j * kKTileBytes, 0);
-      k_dma_one(w, j * kKTileBytes, 1);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int j = 0; j < 3 && j < T; ++j) {
+    const i32x4_t w = tile_words(vk, j, kBC);
+    k_dma_one(w, j * kKTileBytes, 0);
+    k_dma_one(w, j * kKTileBytes, 1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   {
-    const int t2 = min(2, T - 1);
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, t2);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, min(2, T - 1), kBC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-    if constexpr (FP8) {
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(vk, t2);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fetch_k_one(rk, i);
-    }
   }
 
   // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
-  // (fp8: widened to bf16, exact)
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
   if constexpr (FUSEQ) {
-    load_q_fused<FP8>(qf, a, qbase, vq.bytes, vq.row, q_row, hi, FP8 ? a.q_scale[bh] : 1.f);
+    load_q_fused(qf, a, vq, q_row, hi);
   } else {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, vq.bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * kElem);
-      if constexpr (FP8) {
-        qf[kk] = __builtin_bit_cast(bf16x8_t, e4m3x8_to_bf16x8(__builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0)));
-      } else {
-        qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      }
+      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
   }
 
@@ -602,11 +410,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // half-step of tile j+1 (softmax, V permutes, first PV fragment reads).
   // Group 1 runs one barrier behind group 0, so in every phase one group is
   // in a matrix half-step and the other in a vector half-step.
-  // Ring traffic of the matrix half-step of tile j: write V^T tile j+2 (fp8:
-  // and K tile j+2, widened there) to LDS, fetch V tile j+3 (fp8: K tile
-  // j+3) into VGPRs, copy bf16 K tile j+3 into LDS.  Slot reuse: the V^T and
-  // fp8 K slot of tile j+2 last held tile j-2, read by PV(j-2) (QK^T(j-2))
-  // in matrix half-step j-2 (j-3); the bf16 K slot of tile j+3 last held
+  // Ring traffic of the matrix half-step of tile j: write V^T tile j+2 to
+  // LDS, fetch V tile j+3 into VGPRs, copy K tile j+3 into LDS.  Slot
+  // reuse: the V^T slot of tile j+2 last held tile j-2, read by PV(j-2) in
+  // matrix half-step j-2; the K slot of tile j+3 last held
   // tile j-1, read by QK^T(j-1) in matrix half-step j-2; at least one
   // barrier separates those reads from either group's writes.  Tile indices
   // of the fetches are clamped to T-1: extra copies land in slots no later
@@ -616,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // where in the 32-step matrix pipeline the ring traffic goes: LDS writes
   // of tile j+2, the four V loads of tile j+3, the two K copies (or loads)
   constexpr int kStoreStep = 10, kVLoad0 = 12, kVLoadGap = 4, kKLoad0 = 26, kKLoadGap = 3;
-  // vector half-step tail: permute (fp8: widen) the V (K) tile fetched in
+  // vector half-step tail: permute the V tile fetched in
   // the previous matrix half-step, and request the first PV fragments of
   // the next matrix half-step (V^T slot of tile j, K slot of tile j+1)
   auto vector_tail = [&](int kslot_bytes, int vslot_bytes, bf16x8_t *ring) __attribute__((always_inline)) {
@@ -634,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // slots of tile j+2
     constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
     const int tn = min(j + 3, T - 1);
-    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn);
+    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn, kBC);
     // the vector half-step wrote no LDS, and the fragment reads it issued
     // touch a slot no wave writes before the next barrier: a plain barrier
     // that does not wait for them
@@ -646,25 +453,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       const bf16x8_t f = ring[step % kPre];
       if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
-      if (step == kStoreStep) {
-        store_v(kPlus2);
-        if constexpr (FP8) {
-          // widened here rather than in the vector half-step: keeps 8 VGPRs
-          // free across the barrier, at the cost of 16 VALU ops (fp8 only)
-          prepare_k();
-          store_k(kPlus2);
-        }
-      }
+      if (step == kStoreStep) store_v(kPlus2);
       if (step >= kVLoad0 && step < kVLoad0 + 4 * kVLoadGap && (step - kVLoad0) % kVLoadGap == 0)
         fetch_v_one(rvn, (step - kVLoad0) / kVLoadGap);
-      if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) {
-        const int i = step == kKLoad0 ? 0 : 1;
-        if constexpr (FP8) {
-          fetch_k_one(tile_rsrc(vk, tn), i);
-        } else {
-          k_dma_one(tile_words(vk, tn), kPlus3, i);
-        }
-      }
+      if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) k_dma_one(tile_words(vk, tn, kBC), kPlus3, step == kKLoad0 ? 0 : 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -704,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
     l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
   }
-  const float inv = o_scale / l_run;
+  const float inv = 1.0f / l_run;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -718,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     }
 }
 
-template <bool FP8, bool FUSEQ, bool STRIDED>
+template <bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.N + kBR - 1) / kBR;
   const int64_t grid = ntiles * a.BH;
@@ -730,28 +522,24 @@ hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FP8, FUSEQ, STRIDED>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<FUSEQ, STRIDED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<FP8, FUSEQ, STRIDED>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<FUSEQ, STRIDED>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward(const ForwardArgs &a, bool fp8, bool fused, bool strided, hipStream_t s) {
-  const int v = (fp8 ? 4 : 0) | (fused ? 2 : 0) | (strided ? 1 : 0);
+hipError_t launch_forward_bf16(const ForwardArgs &a, bool fused, bool strided, hipStream_t s) {
+  const int v = (fused ? 2 : 0) | (strided ? 1 : 0);
   switch (v) {
-    case 0: return launch<false, false, false>(a, s);
-    case 1: return launch<false, false, true>(a, s);
-    case 2: return launch<false, true, false>(a, s);
-    case 3: return launch<false, true, true>(a, s);
-    case 4: return launch<true, false, false>(a, s);
-    case 5: return launch<true, false, true>(a, s);
-    case 6: return launch<true, true, false>(a, s);
-    default: return launch<true, true, true>(a, s);
+    case 0: return launch<false, false>(a, s);
+    case 1: return launch<false, true>(a, s);
+    case 2: return launch<true, false>(a, s);
+    default: return launch<true, true>(a, s);
   }
 }
 

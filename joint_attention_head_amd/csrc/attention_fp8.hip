@@ -1,0 +1,557 @@
+// Non-causal joint attention O = softmax(Q K^T * scale) V on the gfx950
+// fp8 matrix cores: OCP E4M3 queries, keys, values and probabilities,
+// v_mfma_f32_32x32x64_f8f6f4 with fp32 accumulation, bf16 output.
+//
+// FP8 for both the QK^T and the P.V operands is the attention precision the
+// NVIDIA blog post "Speed up image generation with FLUX 3 Image Klein on
+// NVIDIA Blackwell GPUs" selects in section "Quantized and sparse
+// attention".  The structure follows the bf16 kernel (attention.hip):
+//
+//  * Workgroup = 8 waves = 256 query rows of one (b,h); wave w owns 32 rows
+//    and computes S^T = K Q^T (a lane owns query lane % 32 and 16 of every
+//    32 keys), so the softmax row state is lane-local up to one exchange
+//    with lane ^ 32.  Queries stay in VGPRs as E4M3 codes: 64 bytes a lane,
+//    the B operand of two MFMAs (64 head dims each) per 32 keys.
+//  * O^T = V^T P^T takes P straight from registers as the B operand: the
+//    32 keys a lane holds for a 64-key tile ({32 kb + 8 m + 4 h + r},
+//    h = lane / 32) become k-slots 32 h + 16 kb + 4 m + r, and V^T rows in
+//    LDS list the keys in that slot order, so each operand is two
+//    ds_read_b128 per lane.
+//  * P is stored as e4m3(p'), p' = 2^6 p relative to the row's running
+//    shift: every p' stays <= 2^8 < 448 (the shift moves when a score would
+//    pass 2^8), and values down to p = 2^-12 keep the full 3-bit mantissa.
+//    l sums the fp32 p'; O / l is unchanged by the factor.
+//  * Ping-pong: two groups of four waves, one wave of each group per SIMD;
+//    in every phase one group runs its matrix half-step (PV of the current
+//    tile, QK^T of the next: 8 MFMAs of 64 cycles, raised wave priority)
+//    while the other runs the online softmax.
+//  * K tiles (row = key, 128 B) arrive by direct global -> LDS copies three
+//    tiles ahead; V tiles go global -> VGPR -> byte-transposed -> LDS two
+//    tiles ahead.  Both rings have 4 slots of 8 KiB.
+//  * Scales: per-(b,h) scales of q, k fold into the softmax scale and the
+//    scale of v into the final normalisation.  The fused form (FUSEQ) reads
+//    raw E4M3 queries, applies RMSNorm + RoPE in fp32 and re-encodes each
+//    query with its own scale amax / 448 (so c is per lane).
+#include "attn_common.h"
+
+#include <atomic>
+
+namespace fluxattn {
+namespace {
+
+using namespace attn;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBR = kWaves * 32;                  // query rows per workgroup
+constexpr int kBC = 64;                           // keys per tile
+constexpr int kSlots = 4;                         // per ring (K and V^T)
+constexpr int kKTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes)
+constexpr int kVTileBytes = kHeadDim * kBC;       // 8 KiB, row = head dim (64 codes)
+constexpr int kVRingOffset = kSlots * kKTileBytes;
+constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 64 KiB
+// p' = 2^kPExp p; the shift keeps p' <= 2^(kPExp + kShiftAt - kPExp) = 2^8
+constexpr float kPExp = 6.f;
+constexpr float kShiftAt = 8.f;
+
+// LDS layouts.
+//  K tile : row = key (128 B = 8 chunks of 16 B); chunk c of key r sits at
+//           c ^ ((r >> 1) & 7), so the 16 keys one ds_read_b128 phase reads
+//           hit 16 distinct 16-byte bank groups.
+//  V^T tile: row = head dim d (64 B = 64 keys in slot order, 4 chunks);
+//           chunk c at c ^ (((d >> 2) ^ d) & 3).
+__device__ __forceinline__ int k_off(int key, int ch) { return key * 128 + ((ch ^ ((key >> 1) & 7)) << 4); }
+__device__ __forceinline__ int vt_off(int d, int ch) { return d * 64 + ((ch ^ (((d >> 2) ^ d) & 3)) << 4); }
+// k-slot of key 32 kb + 8 m + 4 h + r: 32 h + 16 kb + 4 m + r
+__device__ __forceinline__ int vslot(int key) {
+  return ((key & 4) << 3) | ((key & 32) >> 1) | ((key & 24) >> 1) | (key & 3);
+}
+
+__device__ __forceinline__ i32x8_t lds_frag(const char *p0, const char *p1) {
+  const i32x4_t x = *reinterpret_cast<const i32x4_t *>(p0);
+  const i32x4_t y = *reinterpret_cast<const i32x4_t *>(p1);
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// D = C + A B on E4M3 operands (unit block scales: exponent 127).
+__device__ __forceinline__ f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// D = C + 2^(sb - 127) A B: sb is this lane's E8M0 block scale of B, i.e.
+// of the 32 B elements the lane holds (its column, one half of k).
+__device__ __forceinline__ f32x16_t mfma_f8_bscaled(i32x8_t a, i32x8_t b, f32x16_t c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+// Queries of the fused entry point: raw E4M3 Q times its scale -> RMSNorm
+// over the 128 dims -> rotation of each adjacent pair -> E4M3 codes of
+// Q' * g * 2^-e with g = softmax scale * log2 e * (k scale) and e the
+// smallest integer that keeps every code within 448 (e = ceil(log2(amax g /
+// 448))): the QK^T MFMA with B block scale 2^e then yields the base-2
+// logits c*S directly, and the largest code of the query lies in (224, 448].
+// Returns the E8M0 scale 127 + e in `sb`.  The lane holds dims
+// 64 kk + 32 hi + (0..31); the other 64 are in lane ^ 32.
+__device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const ForwardArgs &a, const HeadView &vq,
+                                             int q_row, int hi, float in_scale, float g) {
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
+  u32x4_t raw[4];   // raw[2 kk + t]: dims 64 kk + 32 hi + 16 t + (0..15)
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    raw[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rq, (uint32_t)q_row * vq.row + (uint32_t)(64 * (c >> 1) + 32 * hi + 16 * (c & 1)),
+                                             0, 0));
+  float x[64];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[c][w], false);
+      const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[c][w], true);
+      x[16 * c + 4 * w + 0] = lo[0] * in_scale;
+      x[16 * c + 4 * w + 1] = lo[1] * in_scale;
+      x[16 * c + 4 * w + 2] = up[0] * in_scale;
+      x[16 * c + 4 * w + 3] = up[1] * in_scale;
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) ss = fmaf(x[i], x[i], ss);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
+    ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
+  }
+  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  // rows past N belong to no token: any valid row serves, their outputs are
+  // never stored
+  const int tok = min(q_row, a.N - 1);
+  const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
+  const float *w_q = stream_weights(a, tok);
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int d0 = 64 * (c >> 1) + 32 * hi + 16 * (c & 1);   // first dim of this chunk
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 w = *reinterpret_cast<const float4 *>(w_q + d0 + 4 * q4);
+      const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float sn, cs;
+        pair_rotation(a, pos, (d0 + 4 * q4 + 2 * m) >> 1, sn, cs);
+        const int i = 16 * c + 4 * q4 + 2 * m;
+        const float u = x[i] * wv[2 * m] * rstd;
+        const float v = x[i + 1] * wv[2 * m + 1] * rstd;
+        x[i] = u * cs - v * sn;
+        x[i + 1] = u * sn + v * cs;
+        amax = fmaxf(amax, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+      }
+    }
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(amax), __float_as_int(amax), false, false);
+    amax = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+  }
+  // e = ceil(log2 v) for v = amax g / 448 = m 2^E, m in [0.5, 1)
+  const float v = amax * g * (1.0f / 448.f);
+  int e = 0;
+  if (v > 0.f) {
+    e = __builtin_amdgcn_frexp_expf(v);
+    if (__builtin_amdgcn_frexp_mantf(v) == 0.5f) e -= 1;
+    e = min(max(e, -120), 120);
+  }
+  sb = 127 + e;
+  const float inv = g * __builtin_ldexpf(1.0f, -e);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = 32 * kk + 4 * u;
+      // |x * inv| <= amax g 2^-e <= 448 up to fp32 rounding, which rounds
+      // back to 448
+      qf[kk][u] = (int)f32x4_to_e4m3(x[i] * inv, x[i + 1] * inv, x[i + 2] * inv, x[i + 3] * inv);
+    }
+}
+
+template <bool FUSEQ, bool STRIDED>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int simd_of_wave[kWaves];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+
+  const int order = pingpong_order(simd_of_wave, wave, lane);
+  const int group = order & 1;
+  const int gw = order >> 1;                   // wave index inside the group
+  const int rank = gw * 64 + lane;             // 0..255 inside the group
+
+  const int ntiles = (N + kBR - 1) / kBR;
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int bh = logical / ntiles;
+  const int qt = logical - bh * ntiles;
+
+  const HeadView vq = head_view<STRIDED>(a.q, a.sq, 1, bh, a.H, N);
+  const HeadView vk = head_view<STRIDED>(a.k, a.sk, 1, bh, a.H, N);
+  const HeadView vv = head_view<STRIDED>(a.v, a.sv, 1, bh, a.H, N);
+  const HeadView vo = head_view<STRIDED>(a.o, a.so, 2, bh, a.H, N);
+
+  const int T = (N + kBC - 1) / kBC;
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
+
+  // ---- lane constants (bytes).  Each group loads half of every tile:
+  // keys [32 g, 32 g + 32).
+  //  V: thread `rank` owns keys 32 g + 4 kg .. +3 (kg = rank % 8) at head
+  //     dims 4 dq .. +3 (dq = rank / 8): load i reads key 32 g + 4 kg + i;
+  //     the transposed 4x4 byte block goes to V^T rows 4 dq + jj, where the
+  //     four keys occupy four consecutive slots.
+  const int kg = rank & 7, dq = rank >> 3;
+  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq);
+  uint32_t v_goffs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v_goffs[i] = v_goff + (uint32_t)i * vv.row;
+  uint32_t v_soff[4];
+  {
+    const int s0 = vslot(32 * group + 4 * kg);   // multiple of 4
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v_soff[jj] = (uint32_t)(kVRingOffset + vt_off(4 * dq + jj, s0 >> 4) + (s0 & 15));
+  }
+  //  K by direct copies: wave gw of group g copies keys 32 g + 8 gw .. +8
+  //     with one buffer_load_dwordx4 ... lds; lane l fetches the chunk the
+  //     swizzle puts at LDS row 32 g + 8 gw + l / 8, chunk position l % 8.
+  const int krow = 32 * group + 8 * gw + (lane >> 3);
+  const uint32_t k_dgoff = (uint32_t)krow * vk.row + (uint32_t)(16 * ((lane & 7) ^ ((krow >> 1) & 7)));
+  const uint32_t k_m0 = lds_base + 128u * (uint32_t)(32 * group + 8 * gw);
+  //  MFMA fragments (32 bytes = two chunks each): K (kk) row l32, chunks
+  //     4 kk + 2 hi + t; V^T row l32, chunks 2 hi + t.  Slot, 32-key block
+  //     (4 KiB) and head-dim block (2 KiB) are immediates.
+  uint32_t kf[2][2], vf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) kf[kk][t] = (uint32_t)k_off(l32, 4 * kk + 2 * hi + t);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) vf[t] = (uint32_t)(kVRingOffset + vt_off(l32, 2 * hi + t));
+
+  // ---- ring traffic helpers
+  uint32_t vraw[4];       // key 32 g + 4 kg + i, dims 4 dq .. +3
+  uint32_t vt_data[4];    // V^T row 4 dq + jj, keys' slots s0 .. s0 + 3
+  auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
+    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim);
+    vraw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  };
+  // 4x4 byte transpose (vector half-step work)
+  auto prepare_v = [&]() __attribute__((always_inline)) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x07030602u);
+    vt_data[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    vt_data[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    vt_data[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    vt_data[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+  };
+  auto store_v = [&](int slot_bytes) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) *reinterpret_cast<uint32_t *>(lds + v_soff[jj] + slot_bytes) = vt_data[jj];
+  };
+  auto k_dma = [&](const i32x4_t &words, uint32_t slot_bytes) __attribute__((always_inline)) {
+    const uint32_t m0 = k_m0 + slot_bytes;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(k_dgoff), "s"(words)
+        : "memory");
+  };
+
+  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1, 2 in
+  // LDS; V tile 2 in registers.
+  for (int j = 0; j < 2 && j < T; ++j) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j, kBC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
+    prepare_v();
+    store_v(j * kVTileBytes);
+  }
+  for (int j = 0; j < 3 && j < T; ++j) k_dma(tile_words(vk, j, kBC), j * kKTileBytes);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, min(2, T - 1), kBC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
+  }
+
+  // ---- queries: qf[kk] = codes of dims 64 kk + 32 hi .. +32 of this
+  // lane's query; c = softmax scale * log2 e * (q scale) * (k scale)
+  const int q_row = qt * kBR + wave * 32 + l32;
+  i32x8_t qf[2];
+  float qs = 1.f;
+  int qsb = 127;   // fused: E8M0 B scale of the QK^T MFMAs, c folded in
+  if constexpr (FUSEQ) {
+    load_q_fused(qf, qsb, a, vq, q_row, hi, a.q_scale[bh], a.scale_log2 * a.k_scale[bh]);
+  } else {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)(64 * kk + 32 * hi);
+      const i32x4_t x = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      const i32x4_t y = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+      qf[kk] = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    qs = a.q_scale[bh];
+  }
+  // unfused: x = c*S - b by one FMA per score; fused: the MFMA's B scale
+  // applies c and its accumulator starts at -b (`bias`)
+  const float c = a.scale_log2 * qs * a.k_scale[bh];
+  const float o_scale = a.v_scale[bh];
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  f32x16_t s[2];
+  i32x8_t pf;              // P^T operand: byte 16 kb + r = p' of s[kb][r]
+  float b_run = 0.f;       // this row's running shift, base-2 units
+  f32x16_t bias = {};      // fused: -b_run in every element
+  float l_part[2] = {0.f, 0.f};
+  const f32x16_t zero = {};
+
+  // Matrix half-step as an 8-step software pipeline: steps 0..3 are PV of
+  // the current tile (head-dim block db = step), steps 4..7 QK^T of the
+  // next tile (kk = (step-4)/2, 32-key block kb = (step-4)%2).  Operand
+  // step+kPre is requested from LDS before MFMA step is issued.
+  constexpr int kPre = 2;
+  auto frag = [&](int step, int kslot_bytes, int vslot_bytes) __attribute__((always_inline)) -> i32x8_t {
+    if (step >= 4) {
+      const int kk = (step - 4) >> 1, kb = (step - 4) & 1;
+      return lds_frag(lds + kf[kk][0] + (kslot_bytes + kb * 4096), lds + kf[kk][1] + (kslot_bytes + kb * 4096));
+    }
+    return lds_frag(lds + vf[0] + (vslot_bytes + step * 2048), lds + vf[1] + (vslot_bytes + step * 2048));
+  };
+  auto matrix_step = [&](int step, i32x8_t f) __attribute__((always_inline)) {
+    if (step >= 4) {
+      const int kk = (step - 4) >> 1, kb = (step - 4) & 1;
+      if constexpr (FUSEQ) {
+        s[kb] = mfma_f8_bscaled(f, qf[kk], kk ? s[kb] : bias, qsb);
+      } else {
+        s[kb] = mfma_f8(f, qf[kk], kk ? s[kb] : zero);
+      }
+    } else {
+      o[step] = mfma_f8(f, pf, o[step]);
+    }
+  };
+
+  // Online softmax of tile j (see the header comment): x = c*S - b by one
+  // FMA per score, p' = 2^x.  The row maximum is scanned only when the
+  // lane's sum of p' (>= each of them) exceeds 2^8, and on the first tile;
+  // b moves so that the maximum lands at 2^6 when it passes 2^8 (first
+  // tile: always), with O and l rescaled.
+  auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value != 0;
+    if constexpr (!FUSEQ) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
+    }
+    if (j * kBC + kBC > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N) s[kb][r] = -INFINITY;
+        }
+    }
+    float t[2];
+    auto exps = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float e0 = __builtin_amdgcn_exp2f(s[kb][4 * u + 0]);
+          const float e1 = __builtin_amdgcn_exp2f(s[kb][4 * u + 1]);
+          const float e2 = __builtin_amdgcn_exp2f(s[kb][4 * u + 2]);
+          const float e3 = __builtin_amdgcn_exp2f(s[kb][4 * u + 3]);
+          acc += (e0 + e1) + (e2 + e3);
+          pf[4 * kb + u] = (int)f32x4_to_e4m3(e0, e1, e2, e3);
+        }
+        t[kb] = acc;
+      }
+    };
+    if constexpr (!kFirst) exps();
+    const float tot = t[0] + t[1];
+    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= 256.f)) != 0) {
+      float mq[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float m = fmaxf(s[kb][0], s[kb][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) m = fmaxf(m, s[kb][r]);
+        mq[kb] = m;
+      }
+      float mx = fmaxf(mq[0], mq[1]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+        mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
+      }
+      if (kFirst || __builtin_amdgcn_ballot_w64(mx > kShiftAt) != 0) {
+        // first tile: any shift (mx is finite: key 0 is in the tile)
+        const float d = kFirst ? mx - kPExp : fmaxf(mx - kPExp, 0.f);
+        b_run += d;
+        if constexpr (FUSEQ) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bias[i] = -b_run;
+        }
+        if constexpr (!kFirst) {
+          const float alpha = __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+          for (int g = 0; g < 2; ++g) l_part[g] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= d;
+        exps();
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) l_part[g] += t[g];
+    // keep the exponentials in this (vector) half-step
+    asm volatile("" : "+v"(pf));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) asm volatile("" : "+v"(l_part[g]));
+  };
+
+  // Schedule and ring reuse as in the bf16 kernel: QK^T(0), vector
+  // half-step of tile 0, then per tile j a matrix half-step (PV(j),
+  // QK^T(j+1)) and the vector half-step of tile j+1; group 1 runs one
+  // barrier behind group 0.  Ring traffic of matrix half-step j: write V^T
+  // tile j+2, fetch V tile j+3 into VGPRs, copy K tile j+3 into LDS.  The
+  // V^T slot of tile j+2 last held tile j-2 (read by PV(j-2) in matrix
+  // half-step j-2) and the K slot of tile j+3 last held tile j-1 (read by
+  // QK^T(j-1) in matrix half-step j-2): at least one barrier separates
+  // those reads from either group's writes.  Fetch indices are clamped to
+  // T-1; extra copies land in slots no later step reads.  The vmcnt wait in
+  // each vector half-step retires the previous matrix half-step's loads.
+  constexpr int kStoreStep = 0, kVLoad0 = 1, kKLoadStep = 5;
+  auto vector_tail = [&](int kslot_bytes, int vslot_bytes, i32x8_t *ring) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    prepare_v();
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) ring[i] = frag(i, kslot_bytes, vslot_bytes);
+  };
+  auto iteration = [&](int j, auto slot, i32x8_t *ring) __attribute__((always_inline)) {
+    constexpr int R = decltype(slot)::value;
+    constexpr int kCur = R * kKTileBytes;                       // V^T slot of tile j (same offset in both rings)
+    constexpr int kNext = ((R + 1) % kSlots) * kKTileBytes;    // slots of tile j+1
+    constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // V^T slot of tile j+2
+    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
+    const int tn = min(j + 3, T - 1);
+    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn, kBC);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+      const i32x8_t f = ring[step % kPre];
+      if (step + kPre < 8) ring[step % kPre] = frag(step + kPre, kNext, kCur);
+      matrix_step(step, f);
+      if (step == kStoreStep) store_v(kPlus2);
+      if (step >= kVLoad0 && step < kVLoad0 + 4) fetch_v_one(rvn, step - kVLoad0);
+      if (step == kKLoadStep) k_dma(tile_words(vk, tn, kBC), kPlus3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // the QK^T MFMAs belong to this half-step: without this use the
+    // compiler sinks them past the barrier into the softmax branch
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    __syncthreads();
+    if (j + 1 < T) {
+      softmax(j + 1, Slot<0>{});
+      vector_tail(((R + 2) % kSlots) * kKTileBytes, kNext, ring);
+    }
+  };
+
+  __syncthreads();
+  if (group == 1) __syncthreads();
+#pragma unroll
+  for (int step = 4; step < 8; ++step) matrix_step(step, frag(step, 0, 0));
+  __syncthreads();
+  i32x8_t ring[kPre];
+  softmax(0, Slot<1>{});
+  vector_tail(1 * kKTileBytes, 0, ring);
+  int j = 0;
+  for (; j + kSlots <= T; j += kSlots) {
+    iteration(j, Slot<0>{}, ring);
+    iteration(j + 1, Slot<1>{}, ring);
+    iteration(j + 2, Slot<2>{}, ring);
+    iteration(j + 3, Slot<3>{}, ring);
+  }
+  if (j < T) iteration(j, Slot<0>{}, ring);
+  if (j + 1 < T) iteration(j + 1, Slot<1>{}, ring);
+  if (j + 2 < T) iteration(j + 2, Slot<2>{}, ring);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (group == 0) __syncthreads();
+
+  // ---- epilogue: O * s_v / l, one bf16 rounding; lane holds query l32 and
+  // head dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end drop
+  float l_run = l_part[0] + l_part[1];
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
+    l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
+  }
+  const float inv = o_scale / l_run;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2_t w;
+      w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+      w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      const uint32_t off = (uint32_t)q_row * vo.row + (uint32_t)((32 * db + 8 * g + 4 * hi) * 2);
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+    }
+}
+
+template <bool FUSEQ, bool STRIDED>
+hipError_t launch(const ForwardArgs &a, hipStream_t s) {
+  const int64_t grid = (int64_t)((a.N + kBR - 1) / kBR) * a.BH;
+  // Raise the dynamic-LDS limit once per device (idempotent, so a race
+  // between threads only repeats the call).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_fp8_kernel<FUSEQ, STRIDED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<FUSEQ, STRIDED>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_fp8(const ForwardArgs &a, bool fused, bool strided, hipStream_t s) {
+  const int v = (fused ? 2 : 0) | (strided ? 1 : 0);
+  switch (v) {
+    case 0: return launch<false, false>(a, s);
+    case 1: return launch<false, true>(a, s);
+    case 2: return launch<true, false>(a, s);
+    default: return launch<true, true>(a, s);
+  }
+}
+
+}  // namespace fluxattn

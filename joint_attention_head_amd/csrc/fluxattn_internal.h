@@ -69,10 +69,12 @@ hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
                                 hipStream_t s);
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
                                hipStream_t s);
-// Attention launches.  fused: the Q load applies RMSNorm + RoPE to raw
-// queries.  strided: q, k, v, o follow the strides in the arguments (else
-// contiguous [B, H, N, D]).
-hipError_t launch_forward(const ForwardArgs &a, bool fp8, bool fused, bool strided, hipStream_t s);
+// Attention launches: bf16 inputs on the bf16 matrix cores, E4M3 inputs on
+// the fp8 matrix cores (E4M3 Q, K, V and P).  fused: the Q load applies
+// RMSNorm + RoPE to raw queries.  strided: q, k, v, o follow the strides in
+// the arguments (else contiguous [B, H, N, D]).
+hipError_t launch_forward_bf16(const ForwardArgs &a, bool fused, bool strided, hipStream_t s);
+hipError_t launch_forward_fp8(const ForwardArgs &a, bool fused, bool strided, hipStream_t s);
 
 // Workgroups the forward kernel launches for B*H heads of N tokens.
 int64_t forward_grid_blocks(int64_t BH, int64_t N);

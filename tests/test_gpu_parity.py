@@ -383,8 +383,9 @@ def test_joint_fused_bf16_t2i_2048_sampled():
 
 
 def test_joint_fused_fp8_parity():
-    """fp8 with the fused query prologue; Q' stays in bf16, so the result
-    must also be at least as close as the two-call path (E4M3 Q')."""
+    """fp8 with the fused query prologue (Q' re-encoded in E4M3 per query
+    inside the attention kernel) against the fp64 chain, and close to the
+    two-call path, which reads Q' in E4M3 from the prologue."""
     for inp in (small(1, 2, 64, (16, 16), (8, 8), "fp8"), small(2, 1, 5, (16, 20), None, "fp8", seed=4)):
         args = (dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale),
                 dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
@@ -394,7 +395,10 @@ def test_joint_fused_fp8_parity():
         ref = joint_ref(inp)
         rel = check_close(f64(o), ref, FP8_TOL, f"joint fused fp8 N={inp.q.shape[2]}")
         assert rel < 1e-1
-        assert np.abs(f64(o) - ref).mean() <= np.abs(f64(o2) - ref).mean()
+        check_close(f64(o2), ref, FP8_TOL, f"joint two-call fp8 N={inp.q.shape[2]}")
+        # same operations, Q' encoded with a different scale: the two
+        # results differ by fp8 rounding only
+        assert np.abs(f64(o) - f64(o2)).mean() <= FP8_TOL[1]
 
 
 def test_forward_fp8_parity_tiny_and_ragged():

@@ -221,13 +221,23 @@ def test_joint_ex_bf16_packed_streams_parity(case):
     assert torch.equal(bits(o1), bits(o_ref))
 
 
+FP8_CASES = {
+    "t2i_77+256_B2": (2, 3, 77, (16, 16), None),
+    # three streams at N = 449: E4M3 Q', K' and P alone put the mean error
+    # of a 171-token sequence at about 4.1e-3 (CPU emulation of those
+    # roundings, any seed), the size of the tolerance itself; it falls as
+    # the keys per query grow (2.7e-3 here, 3e-4 at the 33280-token I2I)
+    "i2i_9+320+120": (1, 2, 9, (16, 20), (10, 12)),
+}
+
+
 def test_joint_ex_fp8_packed_streams_parity():
-    for case in ("t2i_77+256_B2", "i2i_9+120+42"):
+    for case, (B, H, n_txt, grid, ref_grid) in FP8_CASES.items():
         _flush(f"joint_ex fp8 packed streams {case}")
-        w, _ = CASES[case]()
-        inp = make_inputs(custom_workload(w.B, w.H, w.n_txt, w.grid, w.ref_grid, "fp8", w.seed + 11))
+        w = custom_workload(B, H, n_txt, grid, ref_grid, "fp8", 12)
+        inp = make_inputs(w)
         starts = stream_starts(w)
-        w_q, w_k = stream_norm_weights(len(starts), seed=w.seed + 11)
+        w_q, w_k = stream_norm_weights(len(starts), seed=w.seed)
         p, views = packed(inp.q.view(torch.uint8), inp.k.view(torch.uint8), inp.v.view(torch.uint8))
         qv, kv, vv = (t.view(torch.float8_e4m3fn) for t in views)
         sc = [dev(s) for s in (inp.q_scale, inp.k_scale, inp.v_scale)]
