@@ -14,8 +14,10 @@ runs the prologue on both and the plain attention kernel.
 Prints one JSON line: TFLOP/s of the step (4*B*H*N^2*d per step), the
 attention kernel's roofline fraction (its own average launch time from HIP
 events on the launch stream), the same figures at N=4608 (FLUX-dev 1024x1024)
-under "also", and the fp64 CPU oracle timed on a bounded sample of the same
-workload under "cpu_baseline".
+under "also", the fp8 path (E4M3 Q/K/V, fp8 matrix cores) on the 2048x2048
+image-to-image workload (B=1, H=24, N = 512 + 2 x 128x128 = 33280) under
+"fp8" with its roofline against the fp8 MFMA peak, and the fp64 CPU oracle
+timed on a bounded sample of the main workload under "cpu_baseline".
 """
 from __future__ import annotations
 
@@ -30,33 +32,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_t2i_2048_hbm_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "joint_attention_head_amd", "csrc", f)
-                  for f in ("attention.hip", "fluxattn_internal.h")]
+CSRC = os.path.join(ROOT, "joint_attention_head_amd", "csrc")
+# rocprofv3 counter summaries of the attention kernels, and the sources each
+# kernel is built from (a summary only counts while they are unchanged)
+TRAFFIC = {
+    "bf16": (os.path.join(ROOT, "profiles", "attn_fwd_bf16_t2i_2048_hbm_traffic.txt"),
+             ("attention.hip", "attn_common.h", "fluxattn_internal.h")),
+    "fp8": (os.path.join(ROOT, "profiles", "attn_fwd_fp8_i2i_2048_hbm_traffic.txt"),
+            ("attention_fp8.hip", "attn_common.h", "fluxattn_internal.h")),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str = "bf16") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in TRAFFIC[kind][1]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path: str):
+def measured_traffic(path: str, kind: str = "bf16"):
     """HBM bytes per forward launch from the committed rocprofv3 counter
     summary, or None if the kernel source changed since it was taken or the
     summary covers the other kernel variant."""
-    if not os.path.exists(TRAFFIC_FILE):
+    traffic_file = TRAFFIC[kind][0]
+    if not os.path.exists(traffic_file):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(traffic_file) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash() or vals.get("path", "unfused") != path:
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kind) or vals.get("path", "unfused") != path:
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -71,6 +81,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="t2i_2048_cfg")
     p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
+    p.add_argument("--fp8", default="i2i_2048", help="fp8 workload ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--path", choices=("fused", "unfused"), default="fused")
@@ -87,25 +98,45 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
 
     w = WORKLOADS[name]
     inp = make_inputs(w)
+    fp8 = w.dtype == "fp8"
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     w_q, w_k, pos = inp.w_q.to(dev), inp.w_k.to(dev), inp.pos.to(dev)
-    qn, kn, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    if fp8:
+        sq, sk, sv = (t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale))
+        sqn, skn = torch.empty_like(sq), torch.empty_like(sk)
     stream = torch.cuda.current_stream()
+
+    def prologue():
+        if fp8 and path == "fused":
+            fa.fluxattn_qk_norm_rope_fp8(None, k, None, sk, None, w_k, pos, k_out=kn, k_scale_out=skn, stream=stream)
+        elif fp8:
+            fa.fluxattn_qk_norm_rope_fp8(q, k, sq, sk, w_q, w_k, pos, q_out=qn, k_out=kn, q_scale_out=sqn,
+                                         k_scale_out=skn, stream=stream)
+        elif path == "fused":
+            fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos, k_out=kn, stream=stream)
+        else:
+            fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos, q_out=qn, k_out=kn, stream=stream)
+
+    def attention():
+        if fp8 and path == "fused":
+            fa.fluxattn_forward_fused_fp8(q, kn, v, sq, skn, sv, w_q, pos, o=o, stream=stream)
+        elif fp8:
+            fa.fluxattn_forward_fp8(qn, kn, v, sqn, skn, sv, o=o, stream=stream)
+        elif path == "fused":
+            fa.fluxattn_forward_fused_bf16(q, kn, v, w_q, pos, o=o, stream=stream)
+        else:
+            fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if path == "fused":
-            fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos, k_out=kn, stream=stream)
-        else:
-            fa.fluxattn_qk_norm_rope_bf16(q, k, w_q, w_k, pos, q_out=qn, k_out=kn, stream=stream)
+        prologue()
         if ev is not None:
             ev[1].record(stream)
-        if path == "fused":
-            fa.fluxattn_forward_fused_bf16(q, kn, v, w_q, pos, o=o, stream=stream)
-        else:
-            fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
+        attention()
         if ev is not None:
             ev[2].record(stream)
 
@@ -125,8 +156,9 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
     assert torch.isfinite(o).all().item()
     flops = w.flops
     # read + write K (fused path) or Q and K
-    prologue_bytes = (2.0 if path == "fused" else 4.0) * w.B * w.H * w.N * 128 * 2
-    attn_min_bytes = 4.0 * w.B * w.H * w.N * 128 * 2      # read Q, K, V, write O once
+    esize = 1 if fp8 else 2
+    prologue_bytes = (2.0 if path == "fused" else 4.0) * w.B * w.H * w.N * 128 * esize
+    attn_min_bytes = w.B * w.H * w.N * 128 * (3.0 * esize + 2)   # read Q, K, V, write bf16 O once
     t_fwd = sum(fwd) / len(fwd)
     t_pro = sum(pro) / len(pro)
     res = {
@@ -142,6 +174,8 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
         "flops": flops,
     }
     del q, k, v, qn, kn, o
+    if fp8:
+        del sq, sk, sv, sqn, skn
     torch.cuda.empty_cache()
     return res
 
@@ -216,6 +250,32 @@ def main():
             "prologue_gbs": round(r["prologue_gbs"], 1),
         }
         print(f"bench: {args.also} forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+    fp8 = None
+    if args.fp8:
+        r = run_gpu(args.fp8, args.steps, args.warmup, args.path)
+        w = r["workload"]
+        fp8 = {
+            "workload": f"{w.name}: 2048x2048 image-to-image, B={w.B} H={w.H} "
+                        f"N={w.n_txt}+{w.grid[0]}x{w.grid[1]}+{w.ref_grid[0]}x{w.ref_grid[1]}={w.N} d=128, "
+                        "E4M3 q/k/v with per-(b,h) scales, bf16 output, prologue + attention",
+            "value": round(r["value"], 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(r["ms_per_step"], 4),
+            "dtype": "fp8-e4m3",
+            "roofline": {
+                "kernel": "attn_fwd_fp8_kernel (E4M3 MFMA, %s)" % (
+                    "fused query prologue" if args.path == "fused" else "plain"),
+                "bound": "mfma",
+                "achieved": round(r["forward_tflops"], 2),
+                "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(r["forward_tflops"] / FP8_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.path, "fp8"),
+                "launch_ms": round(r["forward_ms"], 4),
+            },
+            "prologue_gbs": round(r["prologue_gbs"], 1),
+        }
+        print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
     if args.calibrate_copy:
         calibrate_copy()
     cpu = None
@@ -264,6 +324,7 @@ def main():
             "launch_us": round(main_res["prologue_us"], 2),
         },
         "also": also,
+        "fp8": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -157,6 +157,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 
   // ---- per-head base pointers, token-row pitches and buffer extents
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 2, bh, a.H, N);
+  // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
+  // (first, so the fused transform's temporaries overlap no other state)
+  const int q_row = qt * kBR + wave * 32 + l32;
+  bf16x8_t qf[8];
+  if constexpr (FUSEQ) {
+    load_q_fused(qf, a, vq, q_row, hi);
+  } else {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    }
+  }
+
   const HeadView vk = head_view<STRIDED>(a.k, a.sk, 2, bh, a.H, N);
   const HeadView vv = head_view<STRIDED>(a.v, a.sv, 2, bh, a.H, N);
   const HeadView vo = head_view<STRIDED>(a.o, a.so, 2, bh, a.H, N);
@@ -263,20 +278,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, min(2, T - 1), kBC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-  }
-
-  // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
-  const int q_row = qt * kBR + wave * 32 + l32;
-  bf16x8_t qf[8];
-  if constexpr (FUSEQ) {
-    load_q_fused(qf, a, vq, q_row, hi);
-  } else {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
   }
 
   f32x16_t o[4];
