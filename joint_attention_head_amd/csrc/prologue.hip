@@ -14,6 +14,8 @@
 // writes one contiguous 4 KiB (bf16) or 2 KiB (fp8) span.
 #include "fluxattn_internal.h"
 
+#include <algorithm>
+
 namespace fluxattn {
 namespace {
 
@@ -180,6 +182,23 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(const float *f) {
   return (uint32_t)w;
 }
 
+// fp8 rows are 128 B: 8 lanes per token, 16 codes (8 rotation pairs) per
+// lane, so every lane moves 16 bytes per load and store; 32 tokens per block.
+// The (b,h) rows are split over grid.y in chunks of a.bh_chunk (16, more
+// only where grid.y would pass its limit), which gives the half-size fp8
+// stream enough blocks in flight.
+constexpr int kLanes8 = 8;
+constexpr int kTokensPerBlock8 = kThreads / kLanes8;
+constexpr int kChunk8 = 16;
+constexpr int64_t kMaxGridY = 65535;
+
+__device__ __forceinline__ float row8_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+  return x;
+}
+
 __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, RopeTable t) {
   const int lane = threadIdx.x & 63;
   // Output scale sqrt(D) * max|w| / 448: every output lies within +-448 of it.
@@ -196,19 +215,33 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
     sq = mq > 0.f ? root_d * mq / 448.f : 1.f;
     sk = mk > 0.f ? root_d * mk / 448.f : 1.f;
   }
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int64_t i = threadIdx.x; i < a.BH; i += kThreads) {
       if (a.q_scale_out) a.q_scale_out[i] = sq;
       a.k_scale_out[i] = sk;
     }
   }
-  const int c = threadIdx.x & 15;
-  const int tok = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 4);
-  if (tok >= a.N) return;
+  const int c = threadIdx.x & 7;
+  const int tok = blockIdx.x * kTokensPerBlock8 + (threadIdx.x >> 3);
+  if (tok >= a.N) return;  // the 8 lanes of a token leave together
 
-  float cs[4], sn[4];
-  lane_angles(a, t, tok, c, cs, sn);
+  // the lane's 8 pairs 8c .. 8c+7: angles once per token
+  float cs[8], sn[8];
+  {
+    const int32_t p0 = a.pos[3 * (int64_t)tok + 0];
+    const int32_t p1 = a.pos[3 * (int64_t)tok + 1];
+    const int32_t p2 = a.pos[3 * (int64_t)tok + 2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pr = 8 * c + i;
+      const int ax = t.axis[pr];
+      const int32_t p = ax == 0 ? p0 : (ax == 1 ? p1 : p2);
+      sincosf((float)p * t.freq[pr], &sn[i], &cs[i]);
+    }
+  }
 
+  const int64_t bh_begin = (int64_t)blockIdx.y * a.bh_chunk;
+  const int64_t bh_end = min((int64_t)a.BH, bh_begin + a.bh_chunk);
   const int sid = stream_of(a.streams, tok);
   for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint8_t *src = static_cast<const uint8_t *>(which ? a.k : a.q);
@@ -218,13 +251,19 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
     const float *wp = (which ? a.w_k : a.w_q) + sid * kHeadDim;
     const float *s_in = which ? a.k_scale : a.q_scale;
     const float inv_out = 1.0f / (which ? sk : sq);
-    float w[8];
+    float w[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
+    for (int i = 0; i < 16; ++i) w[i] = wp[16 * c + i];
 
-    const int64_t tin = (int64_t)tok * si.n + 8 * c, tout = (int64_t)tok * so.n + 8 * c;
-    HeadWalk walk{0, 0, 0};
-    for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+    const int64_t tin = (int64_t)tok * si.n + 16 * c, tout = (int64_t)tok * so.n + 16 * c;
+    HeadWalk walk;
+    {
+      const int64_t b = bh_begin / a.H, h = bh_begin - b * a.H;
+      walk.in = b * si.b + h * si.h;
+      walk.out = b * so.b + h * so.h;
+      walk.h = (int32_t)h;
+    }
+    for (int64_t bh0 = bh_begin; bh0 < bh_end; bh0 += kUnroll) {
       int64_t oin[kUnroll], oout[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -232,29 +271,43 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
         oout[u] = walk.out + tout;
         walk.next(si, so, a.H);
       }
-      uint2 x[kUnroll];
+      uint4 x[kUnroll];
       float s[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (bh0 + u < a.BH) {
-          x[u] = *reinterpret_cast<const uint2 *>(src + oin[u]);
+        if (bh0 + u < bh_end) {
+          x[u] = *reinterpret_cast<const uint4 *>(src + oin[u]);
           s[u] = s_in[bh0 + u];
         }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (bh0 + u >= a.BH) break;
-        float f[8];
+        if (bh0 + u >= bh_end) break;
+        float f[16];
         e4m3x4_to_f32(x[u].x, f);
         e4m3x4_to_f32(x[u].y, f + 4);
+        e4m3x4_to_f32(x[u].z, f + 8);
+        e4m3x4_to_f32(x[u].w, f + 12);
+        float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] *= s[u];
-        norm_rope8(f, w, cs, sn, a.eps);
+        for (int i = 0; i < 16; ++i) {
+          f[i] *= s[u];
+          ss = fmaf(f[i], f[i], ss);
+        }
+        ss = row8_sum(ss);
+        const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(f[i] * inv_out, -448.f), 448.f);
-        uint2 y;
+        for (int i = 0; i < 8; ++i) {
+          const float uu = f[2 * i] * w[2 * i] * rstd;
+          const float vv = f[2 * i + 1] * w[2 * i + 1] * rstd;
+          f[2 * i] = fminf(fmaxf((uu * cs[i] - vv * sn[i]) * inv_out, -448.f), 448.f);
+          f[2 * i + 1] = fminf(fmaxf((uu * sn[i] + vv * cs[i]) * inv_out, -448.f), 448.f);
+        }
+        uint4 y;
         y.x = f32x4_to_e4m3(f);
         y.y = f32x4_to_e4m3(f + 4);
-        *reinterpret_cast<uint2 *>(dst + oout[u]) = y;
+        y.z = f32x4_to_e4m3(f + 8);
+        y.w = f32x4_to_e4m3(f + 12);
+        *reinterpret_cast<uint4 *>(dst + oout[u]) = y;
       }
     }
   }
@@ -269,8 +322,10 @@ hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t, hipSt
 }
 
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
-  const dim3 grid((a.N + kTokensPerBlock - 1) / kTokensPerBlock);
-  hipLaunchKernelGGL(prologue_fp8_kernel, grid, dim3(kThreads), 0, s, a, t);
+  PrologueArgs b = a;
+  b.bh_chunk = (int32_t)std::max<int64_t>(kChunk8, (a.BH + kMaxGridY - 1) / kMaxGridY);
+  const dim3 grid((a.N + kTokensPerBlock8 - 1) / kTokensPerBlock8, (unsigned)((a.BH + b.bh_chunk - 1) / b.bh_chunk));
+  hipLaunchKernelGGL(prologue_fp8_kernel, grid, dim3(kThreads), 0, s, b, t);
   return hipGetLastError();
 }
 
