@@ -17,9 +17,8 @@
 //    operand.  The keys a lane holds for one MFMA step are
 //    {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); since keys are summed over,
 //    the V^T operand only has to list the same keys in the same order.  V
-//    tiles are stored transposed in LDS (row = head dim) with bits 2 and 3
-//    of the key swapped inside every group of 16, so that list is one
-//    ds_read_b128 per lane.
+//    tiles sit in LDS as they are in memory (row = key); two transposing
+//    reads (ds_read_b64_tr_b16) give a lane those 8 keys at its head dim.
 //  * Ping-pong: the waves form two groups of four, one wave of each group per
 //    SIMD.  Every phase ends with a workgroup barrier; in each phase one
 //    group runs its matrix half-step (PV of the current tile, QK^T of the
@@ -29,15 +28,14 @@
 //  * The matrix half-step issues no VALU instruction: a VALU op of the MFMA
 //    wave would queue behind the other wave's softmax and hold up the MFMA
 //    stream.  LDS addresses are lane constants plus immediates (the loop is
-//    unrolled over the four ring slots), global loads take per-tile buffer
-//    descriptors built with scalar ops, and the V transpose permutes run in
-//    the vector half-step.
-//  * K tiles and V^T tiles of 64 keys go through two 4-slot LDS rings
-//    (64 KiB each).  Both groups load half of every tile, spread over their
-//    matrix half-steps: K by direct global -> LDS buffer loads, three tiles
-//    ahead; V global -> VGPR, permuted in the next vector half-step and
-//    written to LDS in the matrix half-step after that, two tiles ahead.  Buffer-resource loads return 0 past the end of a
-//    head, so ragged tails need no branches; the softmax masks keys >= N.
+//    unrolled over the four ring slots), and global loads take per-tile
+//    buffer descriptors built with scalar ops.
+//  * K and V tiles of 64 keys go through two 4-slot LDS rings (64 KiB
+//    each).  Both groups copy half of every tile with direct global -> LDS
+//    buffer loads, three tiles ahead, spread over their matrix half-steps;
+//    no tile passes through VGPRs.  Buffer-resource loads return 0 past the
+//    end of a head, so ragged tails need no branches; the softmax masks
+//    keys >= N.
 //  * Online softmax in base 2: one FMA per score gives x = c*S - b (c =
 //    scale * log2 e, b = the row's running shift), then p = 2^x.  The row
 //    maximum is only scanned when the tile's row sum (an upper bound of
@@ -60,28 +58,39 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;                  // query rows per workgroup
 constexpr int kBC = 64;                           // keys per tile
-constexpr int kSlots = 4;                         // per ring (K and V^T)
+constexpr int kSlots = 4;                         // per ring (K and V)
 constexpr int kKTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = key
-constexpr int kVTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = head dim
+constexpr int kVTileBytes = kBC * kHeadDim * 2;   // 16 KiB, row = key
 constexpr int kVRingOffset = kSlots * kKTileBytes;
 constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 128 KiB
 
 using namespace attn;
 
-// LDS layouts (K ring, then V^T ring; 16 KiB per slot).
-//  K tile : row = key (256 B), 16-byte chunk c of the head dim stored at
-//           c ^ (key & 15): the 16 keys one ds_read_b128 phase touches hit 16
-//           distinct bank groups.
-//  V^T tile: row = head dim d (128 B = 64 keys), keys permuted inside every
-//           group of 16 (bits 2 and 3 swapped) so that the 8 keys a lane
-//           feeds one PV MFMA are consecutive; chunk c stored at
-//           c ^ ((d >> 1) & 7).
+// LDS layouts (K ring, then V ring; 16 KiB per slot).
+//  K tile: row = key (256 B), 16-byte chunk c of the head dim stored at
+//          c ^ (key & 15): the 16 keys one ds_read_b128 phase touches hit 16
+//          distinct bank groups.
+//  V tile: row = key (256 B), chunk c stored at c ^ vsw(key), vsw taking
+//          key % 4 to 0, 6, 10, 12.  A transposing read touches 4
+//          consecutive keys x 32 bytes per 16 lanes and 8 keys x 64 bytes per
+//          wave; the swizzle puts every 32-byte piece of one 256-byte bank
+//          row in its own banks.  The swizzle only moves chunks within bits
+//          1..3 of their index and depends on key % 4, so key offsets that
+//          are multiples of 4 stay immediates.
 __device__ __forceinline__ int k_off(int key, int ch) { return key * 256 + ((ch ^ (key & 15)) << 4); }
-__device__ __forceinline__ int vt_off(int d, int ch) { return d * 128 + ((ch ^ ((d >> 1) & 7)) << 4); }
-__device__ __forceinline__ int vperm(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+__device__ __forceinline__ int vsw(int key) { return (0xCA60 >> (4 * (key & 3))) & 15; }
+__device__ __forceinline__ int v_off(int key, int ch) { return key * 256 + ((ch ^ vsw(key)) << 4); }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
+}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// two transposing reads: elements 0..3 from p, 4..7 from p + 2048 (8 keys on)
+__device__ __forceinline__ bf16x8_t lds_read_tr2(const char *p) {
+  typedef __attribute__((address_space(3))) i16x4_t *lp;
+  const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
+  const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 2048));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Queries of the fused entry points: raw Q -> RMSNorm over the 128 dims ->
@@ -182,25 +191,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
   // keys [32 g, 32 g + 32).
-  //  V: thread `rank` owns keys 32 g + 4 kg .. +3 (kg = rank % 8) at head
-  //     dims 4 dq .. +3 (dq = rank / 8): load i reads key 32 g + 4 kg + i,
-  //     and the transposed 4x4 block goes to V^T rows 4 dq + jj.
-  const int kg = rank & 7, dq = rank >> 3;
-  // offset of load i: v_goff + i * vv.row (an immediate for contiguous
-  // tensors; separate registers for strided ones)
-  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq * 2);
-  uint32_t v_goffs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v_goffs[i] = v_goff + (uint32_t)i * vv.row;
-  // (rows 4 dq + 1 and 4 dq + 3 share the swizzle of rows 4 dq and 4 dq + 2
-  // and sit 128 bytes after them)
-  uint32_t v_soff[2];
-  {
-    const int kp = vperm(32 * group + 4 * kg);   // multiple of 4: the 4 keys stay adjacent
-    const int ch = kp >> 3, within = (kp & 7) * 2;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) v_soff[h] = (uint32_t)(kVRingOffset + vt_off(4 * dq + 2 * h, ch) + within);
-  }
   //  K by direct copies: wave gw of group g copies rows
   //     32 g + 8 gw .. +8 with two buffer_load_dwordx4 ... lds; lane l of
   //     copy i fetches the chunk the K swizzle puts at LDS slot row
@@ -213,40 +203,35 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     k_dgoff[i] = (uint32_t)row * vk.row + (uint32_t)(8 * ch * 2);
   }
   const uint32_t k_m0 = lds_base + 256u * (uint32_t)(32 * group + 8 * gw);
-  //  MFMA fragments: K (kk) row l32, chunk 2 kk + hi; V^T (st) row l32,
-  //     chunk 2 st + hi.  Slot, 32-key block and head-dim block are
-  //     immediates.
-  uint32_t kf[8], vf[4];
+  //  V by direct copies of the same rows into the V ring, with its swizzle:
+  //     lane l fetches the chunk that lands at chunk position l % 16
+  uint32_t v_dgoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * group + 8 * gw + 4 * i + (lane >> 4);
+    v_dgoff[i] = (uint32_t)row * vv.row + (uint32_t)(16 * ((lane & 15) ^ vsw(row)));
+  }
+  //  MFMA fragments: K (kk) row l32, chunk 2 kk + hi; slot and 32-key
+  //     block are immediates.
+  uint32_t kf[8], vtr[4];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) kf[kk] = (uint32_t)k_off(l32, 2 * kk + hi);
+  //  PV operand by transposing reads.  Within 16 lanes, lane m of a
+  //     ds_read_b64_tr_b16 receives element m % 4 of the 8-byte pieces that
+  //     lanes m / 4, 4 + m / 4, 8 + m / 4, 12 + m / 4 address.  Lane L
+  //     addresses key 4 (L / 32) + (L / 4) % 4 (+ 16 st + 8 half: slot and
+  //     key offsets are immediates), head dims 32 db + 16 ((L / 16) % 2) +
+  //     4 (L % 4) .. +4; so lane l receives head dim 32 db + l % 32 of keys
+  //     16 st + 8 half + 4 (l / 32) + 0..3, the order of the B operand.
+  {
+    const int row0 = 4 * hi + ((lane >> 2) & 3);
+    const int dh = (lane >> 4) & 1, i4 = lane & 3;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) vf[st] = (uint32_t)(kVRingOffset + vt_off(l32, 2 * st + hi));
+    for (int db = 0; db < 4; ++db)
+      vtr[db] = (uint32_t)(kVRingOffset + v_off(row0, 4 * db + 2 * dh + (i4 >> 1)) + 8 * (i4 & 1));
+  }
 
   // ---- ring traffic helpers
-  u32x2_t vraw[4];        // 4 keys x 4 dims per lane
-  u32x2_t vt_data[4];     // transposed V rows, ready for LDS
-  auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
-    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim * 2);
-    vraw[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  };
-  // VGPR -> transposed rows (vector half-step work)
-  auto prepare_v = [&]() __attribute__((always_inline)) {
-    u32x2_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = vraw[i];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      const int h = jj >> 1;
-      vt_data[jj][0] = __builtin_amdgcn_perm(w[1][h], w[0][h], sel);
-      vt_data[jj][1] = __builtin_amdgcn_perm(w[3][h], w[2][h], sel);
-    }
-  };
-  auto store_v = [&](int slot_bytes) __attribute__((always_inline)) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      *reinterpret_cast<u32x2_t *>(lds + v_soff[jj >> 1] + (slot_bytes + 128 * (jj & 1))) = vt_data[jj];
-  };
   // one of the two direct K copies of this wave: 1 KiB = 4 rows
   auto k_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
     const uint32_t m0 = k_m0 + slot_bytes + 1024u * (uint32_t)i;
@@ -258,27 +243,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
         : "s"(m0), "v"(k_dgoff[i]), "s"(words)
         : "memory");
   };
+  // one of the two direct V copies of this wave
+  auto v_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
+    const uint32_t m0 = k_m0 + kVRingOffset + slot_bytes + 1024u * (uint32_t)i;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(v_dgoff[i]), "s"(words)
+        : "memory");
+  };
 
-  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1, 2 in
-  // LDS; V tile 2 in registers.
-  for (int j = 0; j < 2 && j < T; ++j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j, kBC);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-    prepare_v();
-    store_v(j * kVTileBytes);
-  }
+  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
   for (int j = 0; j < 3 && j < T; ++j) {
     const i32x4_t w = tile_words(vk, j, kBC);
     k_dma_one(w, j * kKTileBytes, 0);
     k_dma_one(w, j * kKTileBytes, 1);
+    const i32x4_t wv = tile_words(vv, j, kBC);
+    v_dma_one(wv, j * kKTileBytes, 0);
+    v_dma_one(wv, j * kKTileBytes, 1);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, min(2, T - 1), kBC);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-  }
 
   f32x16_t o[4];
 #pragma unroll
@@ -296,8 +282,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // block db = s%4), steps 16..31 QK^T of the next tile (kk = (s-16)/2,
   // 32-key block kb = (s-16)%2).  Fragment s+kPre is requested from LDS
   // before MFMA s is issued, and scheduling fences keep that order.  The
-  // V^T tile of the PV steps is complete before the half-step starts, so
-  // the first kPre fragments are requested before the barrier.
+  // V tile of the PV steps is complete before the half-step starts, so the
+  // first kPre fragments are requested before the barrier.  A PV fragment
+  // is two transposing reads, a QK^T fragment one ds_read_b128.
   constexpr int kPre = 6;
   auto frag = [&](int step, int kslot_bytes, int vslot_bytes) __attribute__((always_inline)) -> bf16x8_t {
     if (step >= 16) {
@@ -305,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       return lds_read_b128(lds + kf[kk] + (kslot_bytes + kb * 32 * 256));
     }
     const int st = step >> 2, db = step & 3;
-    return lds_read_b128(lds + vf[st] + (vslot_bytes + db * 32 * 128));
+    return lds_read_tr2(lds + vtr[db] + (vslot_bytes + st * 16 * 256));
   };
   auto matrix_step = [&](int step, bf16x8_t f) __attribute__((always_inline)) {
     if (step >= 16) {
@@ -408,28 +395,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 
   // Schedule of each wave: QK^T(0), vector half-step of tile 0, then per
   // tile j a matrix half-step (PV(j), QK^T(j+1)) followed by the vector
-  // half-step of tile j+1 (softmax, V permutes, first PV fragment reads).
-  // Group 1 runs one barrier behind group 0, so in every phase one group is
-  // in a matrix half-step and the other in a vector half-step.
-  // Ring traffic of the matrix half-step of tile j: write V^T tile j+2 to
-  // LDS, fetch V tile j+3 into VGPRs, copy K tile j+3 into LDS.  Slot
-  // reuse: the V^T slot of tile j+2 last held tile j-2, read by PV(j-2) in
-  // matrix half-step j-2; the K slot of tile j+3 last held
-  // tile j-1, read by QK^T(j-1) in matrix half-step j-2; at least one
+  // half-step of tile j+1 (softmax, first fragment reads of the next matrix
+  // half-step).  Group 1 runs one barrier behind group 0, so in every phase
+  // one group is in a matrix half-step and the other in a vector half-step.
+  // Ring traffic of the matrix half-step of tile j: copy K and V tile j+3
+  // into LDS.  Slot reuse: both slots of tile j+3 last held tile j-1, read
+  // by PV(j-1) and QK^T(j-1) in matrix half-steps j-1 and j-2; at least one
   // barrier separates those reads from either group's writes.  Tile indices
-  // of the fetches are clamped to T-1: extra copies land in slots no later
+  // of the copies are clamped to T-1: extra copies land in slots no later
   // step reads.  The vmcnt wait in each vector half-step retires the
-  // previous matrix half-step's loads, so a bf16 K copy is in LDS two
-  // barriers before QK^T first reads it.
-  // where in the 32-step matrix pipeline the ring traffic goes: LDS writes
-  // of tile j+2, the four V loads of tile j+3, the two K copies (or loads)
-  constexpr int kStoreStep = 10, kVLoad0 = 12, kVLoadGap = 4, kKLoad0 = 26, kKLoadGap = 3;
-  // vector half-step tail: permute the V tile fetched in
-  // the previous matrix half-step, and request the first PV fragments of
-  // the next matrix half-step (V^T slot of tile j, K slot of tile j+1)
+  // previous matrix half-step's copies, so a tile is in LDS two barriers
+  // before its first reader.
+  // where in the 32-step matrix pipeline the two V and the two K copies go
+  constexpr int kVLoad0 = 12, kVLoadGap = 6, kKLoad0 = 26, kKLoadGap = 3;
+  // vector half-step tail: retire this wave's copies, then request the
+  // first fragments of the next matrix half-step (V slot of tile j, K slot
+  // of tile j+1)
   auto vector_tail = [&](int kslot_bytes, int vslot_bytes, bf16x8_t *ring) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    prepare_v();
 #pragma unroll
     for (int i = 0; i < kPre; ++i) ring[i] = frag(i, kslot_bytes, vslot_bytes);
   };
@@ -437,12 +420,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // with the ring traffic, then the vector half-step of tile j+1.
   auto iteration = [&](int j, auto slot, bf16x8_t *ring) __attribute__((always_inline)) {
     constexpr int R = decltype(slot)::value;
-    constexpr int kCur = R * kKTileBytes;                       // V^T slot of tile j (same byte offset in both rings)
+    constexpr int kCur = R * kKTileBytes;                       // V slot of tile j (same byte offset in both rings)
     constexpr int kNext = ((R + 1) % kSlots) * kKTileBytes;    // slots of tile j+1
-    constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // slots of tile j+2
     constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
     const int tn = min(j + 3, T - 1);
-    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn, kBC);
     // the vector half-step wrote no LDS, and the fragment reads it issued
     // touch a slot no wave writes before the next barrier: a plain barrier
     // that does not wait for them
@@ -454,9 +435,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       const bf16x8_t f = ring[step % kPre];
       if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
-      if (step == kStoreStep) store_v(kPlus2);
-      if (step >= kVLoad0 && step < kVLoad0 + 4 * kVLoadGap && (step - kVLoad0) % kVLoadGap == 0)
-        fetch_v_one(rvn, (step - kVLoad0) / kVLoadGap);
+      if (step == kVLoad0 || step == kVLoad0 + kVLoadGap) v_dma_one(tile_words(vv, tn, kBC), kPlus3, step == kVLoad0 ? 0 : 1);
       if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) k_dma_one(tile_words(vk, tn, kBC), kPlus3, step == kKLoad0 ? 0 : 1);
       __builtin_amdgcn_sched_barrier(0);
     }
