@@ -18,9 +18,10 @@
 //    LDS list the keys in that slot order, so each operand is two
 //    ds_read_b128 per lane.
 //  * P is stored as e4m3(p'), p' = 2^6 p relative to the row's running
-//    shift: every p' stays <= 2^8 < 448 (the shift moves when a score would
-//    pass 2^8), and values down to p = 2^-12 keep the full 3-bit mantissa.
-//    l sums the fp32 p'; O / l is unchanged by the factor.
+//    shift (a shift puts the row maximum at 2^6): every p' stays <= 448,
+//    the largest finite E4M3 value, and values down to p = 2^-12 keep the
+//    full 3-bit mantissa.  l sums the fp32 p'; O / l is unchanged by the
+//    factor.
 //  * Ping-pong: two groups of four waves, one wave of each group per SIMD;
 //    in every phase one group runs its matrix half-step (PV of the current
 //    tile, QK^T of the next: 8 MFMAs of 64 cycles, raised wave priority)
@@ -50,9 +51,14 @@ constexpr int kKTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes
 constexpr int kVTileBytes = kHeadDim * kBC;       // 8 KiB, row = head dim (64 codes)
 constexpr int kVRingOffset = kSlots * kKTileBytes;
 constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 64 KiB
-// p' = 2^kPExp p; the shift keeps p' <= 2^(kPExp + kShiftAt - kPExp) = 2^8
+// After a shift the row maximum is p' = 2^kPExp.  A tile whose lane sums of
+// p' are all <= kSumOk has every p' <= 448 and needs no maximum; otherwise
+// the shift moves when some p' exceeds 2^kShiftAt.  (A lower kPExp would
+// make the scan rarer still, but sends two more binades of small p' to
+// E4M3 subnormals.)
 constexpr float kPExp = 6.f;
 constexpr float kShiftAt = 8.f;
+constexpr float kSumOk = 448.f;
 
 // LDS layouts.
 //  K tile : row = key (128 B = 8 chunks of 16 B); chunk c of key r sits at
@@ -344,10 +350,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   };
 
   // Online softmax of tile j (see the header comment): x = c*S - b by one
-  // FMA per score, p' = 2^x.  The row maximum is scanned only when the
-  // lane's sum of p' (>= each of them) exceeds 2^8, and on the first tile;
-  // b moves so that the maximum lands at 2^6 when it passes 2^8 (first
-  // tile: always), with O and l rescaled.
+  // FMA per score (fused: by the MFMA's scale and accumulator), p' = 2^x.
+  // The row maximum is scanned only when some lane's sum of p' (>= each of
+  // them) exceeds kSumOk, and on the first tile; b moves so that the maximum
+  // lands at 2^kPExp when it passes 2^kShiftAt (first tile: always), with O
+  // and l rescaled.
   auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value != 0;
     if constexpr (!FUSEQ) {
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
     };
     if constexpr (!kFirst) exps();
     const float tot = t[0] + t[1];
-    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= 256.f)) != 0) {
+    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= kSumOk)) != 0) {
       float mq[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
