@@ -14,9 +14,10 @@
 //    the B operand of two MFMAs (64 head dims each) per 32 keys.
 //  * O^T = V^T P^T takes P straight from registers as the B operand: the
 //    32 keys a lane holds for a 64-key tile ({32 kb + 8 m + 4 h + r},
-//    h = lane / 32) become k-slots 32 h + 16 kb + 4 m + r, and V^T rows in
-//    LDS list the keys in that slot order, so each operand is two
-//    ds_read_b128 per lane.
+//    h = lane / 32) become k-slots 32 h + 16 kb + 4 m + r.  V tiles sit in
+//    LDS as they are in memory (row = key); four transposing byte reads
+//    (ds_read_b64_tr_b8) give a lane its head dim of those keys in that
+//    slot order.
 //  * P is stored as e4m3(p'), p' = 2^6 p relative to the row's running
 //    shift (a shift puts the row maximum at 2^6): every p' stays <= 448,
 //    the largest finite E4M3 value, and values down to p = 2^-12 keep the
@@ -26,13 +27,14 @@
 //    in every phase one group runs its matrix half-step (PV of the current
 //    tile, QK^T of the next: 8 MFMAs of 64 cycles, raised wave priority)
 //    while the other runs the online softmax.
-//  * K tiles (row = key, 128 B) arrive by direct global -> LDS copies three
-//    tiles ahead; V tiles go global -> VGPR -> byte-transposed -> LDS two
-//    tiles ahead.  Both rings have 4 slots of 8 KiB.
+//  * K and V tiles (row = key, 128 B) arrive by direct global -> LDS copies
+//    three tiles ahead; nothing passes through VGPRs.  Both rings have 4
+//    slots of 8 KiB.
 //  * Scales: per-(b,h) scales of q, k fold into the softmax scale and the
 //    scale of v into the final normalisation.  The fused form (FUSEQ) reads
 //    raw E4M3 queries, applies RMSNorm + RoPE in fp32 and re-encodes each
-//    query with its own scale amax / 448 (so c is per lane).
+//    query with its own power-of-two scale, which the QK^T MFMA applies as
+//    its B block scale together with the softmax scale.
 #include "attn_common.h"
 
 #include <atomic>
@@ -46,9 +48,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;                  // query rows per workgroup
 constexpr int kBC = 64;                           // keys per tile
-constexpr int kSlots = 4;                         // per ring (K and V^T)
+constexpr int kSlots = 4;                         // per ring (K and V)
 constexpr int kKTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes)
-constexpr int kVTileBytes = kHeadDim * kBC;       // 8 KiB, row = head dim (64 codes)
+constexpr int kVTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes)
 constexpr int kVRingOffset = kSlots * kKTileBytes;
 constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 64 KiB
 // After a shift the row maximum is p' = 2^kPExp.  A tile whose lane sums of
@@ -64,13 +66,27 @@ constexpr float kSumOk = 448.f;
 //  K tile : row = key (128 B = 8 chunks of 16 B); chunk c of key r sits at
 //           c ^ ((r >> 1) & 7), so the 16 keys one ds_read_b128 phase reads
 //           hit 16 distinct 16-byte bank groups.
-//  V^T tile: row = head dim d (64 B = 64 keys in slot order, 4 chunks);
-//           chunk c at c ^ (((d >> 2) ^ d) & 3).
+//  V tile : row = key (128 B = 8 chunks of 16 B); chunk c of key r sits at
+//           c ^ vsw(r), vsw(r) made of bits 0, 1 and 3 of r.  A transposing
+//           read touches 8 keys (r % 4 = 0..3 at two r / 8) x 16 bytes per
+//           16 lanes and 16 keys x 32 bytes per wave; this puts every
+//           16-byte piece of one pass in its own banks.  Key offsets that
+//           are multiples of 16 stay immediates.
 __device__ __forceinline__ int k_off(int key, int ch) { return key * 128 + ((ch ^ ((key >> 1) & 7)) << 4); }
-__device__ __forceinline__ int vt_off(int d, int ch) { return d * 64 + ((ch ^ (((d >> 2) ^ d) & 3)) << 4); }
-// k-slot of key 32 kb + 8 m + 4 h + r: 32 h + 16 kb + 4 m + r
-__device__ __forceinline__ int vslot(int key) {
-  return ((key & 4) << 3) | ((key & 32) >> 1) | ((key & 24) >> 1) | (key & 3);
+__device__ __forceinline__ int vsw(int key) { return (key & 3) | ((key >> 1) & 4); }
+__device__ __forceinline__ int v_off(int key, int ch) { return key * 128 + ((ch ^ vsw(key)) << 4); }
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+// PV operand: four transposing byte reads, 16 keys apart (2 KiB)
+__device__ __forceinline__ i32x8_t lds_read_tr8x4(const char *p) {
+  typedef __attribute__((address_space(3))) i32x2_t *lp;
+  const i32x2_t a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lp)(p));
+  const i32x2_t b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lp)(p + 2048));
+  const i32x2_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lp)(p + 4096));
+  const i32x2_t d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lp)(p + 6144));
+  const i32x4_t x = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const i32x4_t y = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ i32x8_t lds_frag(const char *p0, const char *p1) {
@@ -206,60 +222,38 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
   // keys [32 g, 32 g + 32).
-  //  V: thread `rank` owns keys 32 g + 4 kg .. +3 (kg = rank % 8) at head
-  //     dims 4 dq .. +3 (dq = rank / 8): load i reads key 32 g + 4 kg + i;
-  //     the transposed 4x4 byte block goes to V^T rows 4 dq + jj, where the
-  //     four keys occupy four consecutive slots.
-  const int kg = rank & 7, dq = rank >> 3;
-  const uint32_t v_goff = (uint32_t)(32 * group + 4 * kg) * vv.row + (uint32_t)(4 * dq);
-  uint32_t v_goffs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v_goffs[i] = v_goff + (uint32_t)i * vv.row;
-  uint32_t v_soff[4];
-  {
-    const int s0 = vslot(32 * group + 4 * kg);   // multiple of 4
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v_soff[jj] = (uint32_t)(kVRingOffset + vt_off(4 * dq + jj, s0 >> 4) + (s0 & 15));
-  }
   //  K by direct copies: wave gw of group g copies keys 32 g + 8 gw .. +8
   //     with one buffer_load_dwordx4 ... lds; lane l fetches the chunk the
   //     swizzle puts at LDS row 32 g + 8 gw + l / 8, chunk position l % 8.
   const int krow = 32 * group + 8 * gw + (lane >> 3);
   const uint32_t k_dgoff = (uint32_t)krow * vk.row + (uint32_t)(16 * ((lane & 7) ^ ((krow >> 1) & 7)));
   const uint32_t k_m0 = lds_base + 128u * (uint32_t)(32 * group + 8 * gw);
-  //  MFMA fragments (32 bytes = two chunks each): K (kk) row l32, chunks
-  //     4 kk + 2 hi + t; V^T row l32, chunks 2 hi + t.  Slot, 32-key block
-  //     (4 KiB) and head-dim block (2 KiB) are immediates.
-  uint32_t kf[2][2], vf[2];
+  //  V by direct copies of the same rows into the V ring, with its swizzle
+  const uint32_t v_dgoff = (uint32_t)krow * vv.row + (uint32_t)(16 * ((lane & 7) ^ vsw(krow)));
+  //  QK^T fragments (32 bytes = two chunks each): K (kk) row l32, chunks
+  //     4 kk + 2 hi + t.  Slot and 32-key block (4 KiB) are immediates.
+  uint32_t kf[2][2], vtr[4];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int t = 0; t < 2; ++t) kf[kk][t] = (uint32_t)k_off(l32, 4 * kk + 2 * hi + t);
+  //  PV operand by transposing byte reads.  Within 16 lanes, lane m of a
+  //     ds_read_b64_tr_b8 receives byte m % 8 of the 8-byte pieces that
+  //     lanes 2 j + m / 8 (j = 0..7) address.  Lane L addresses key
+  //     4 (L / 32) + 8 ((L % 16) / 8) + (L % 16) / 2 % 4 (+ 16 t for read
+  //     t), head dims 32 db + 16 ((L / 16) % 2) + 8 (L % 2) .. +8; so lane
+  //     l receives head dim 32 db + l % 32 of the keys in the k-slot order
+  //     of its P operand.
+  {
+    const int t16 = lane & 15;
+    const int row0 = 4 * hi + 8 * (t16 >> 3) + ((t16 >> 1) & 3);
+    const int dh = (lane >> 4) & 1, i2 = lane & 1;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) vf[t] = (uint32_t)(kVRingOffset + vt_off(l32, 2 * hi + t));
+    for (int db = 0; db < 4; ++db)
+      vtr[db] = (uint32_t)(kVRingOffset + v_off(row0, 2 * db + dh) + 8 * i2);
+  }
 
   // ---- ring traffic helpers
-  uint32_t vraw[4];       // key 32 g + 4 kg + i, dims 4 dq .. +3
-  uint32_t vt_data[4];    // V^T row 4 dq + jj, keys' slots s0 .. s0 + 3
-  auto fetch_v_one = [&](__amdgpu_buffer_rsrc_t r, int i) __attribute__((always_inline)) {
-    const uint32_t off = STRIDED ? v_goffs[i] : v_goff + (uint32_t)(i * kHeadDim);
-    vraw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  };
-  // 4x4 byte transpose (vector half-step work)
-  auto prepare_v = [&]() __attribute__((always_inline)) {
-    const uint32_t lo01 = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x05010400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(vraw[1], vraw[0], 0x07030602u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(vraw[3], vraw[2], 0x07030602u);
-    vt_data[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-    vt_data[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-    vt_data[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-    vt_data[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-  };
-  auto store_v = [&](int slot_bytes) __attribute__((always_inline)) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) *reinterpret_cast<uint32_t *>(lds + v_soff[jj] + slot_bytes) = vt_data[jj];
-  };
   auto k_dma = [&](const i32x4_t &words, uint32_t slot_bytes) __attribute__((always_inline)) {
     const uint32_t m0 = k_m0 + slot_bytes;
     asm volatile(
@@ -270,23 +264,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
         : "s"(m0), "v"(k_dgoff), "s"(words)
         : "memory");
   };
+  auto v_dma = [&](const i32x4_t &words, uint32_t slot_bytes) __attribute__((always_inline)) {
+    const uint32_t m0 = k_m0 + kVRingOffset + slot_bytes;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(v_dgoff), "s"(words)
+        : "memory");
+  };
 
-  // ---- rings, before the loop: V^T tiles 0, 1 and K tiles 0, 1, 2 in
-  // LDS; V tile 2 in registers.
-  for (int j = 0; j < 2 && j < T; ++j) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, j, kBC);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-    prepare_v();
-    store_v(j * kVTileBytes);
+  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
+  for (int j = 0; j < 3 && j < T; ++j) {
+    k_dma(tile_words(vk, j, kBC), j * kKTileBytes);
+    v_dma(tile_words(vv, j, kBC), j * kVTileBytes);
   }
-  for (int j = 0; j < 3 && j < T; ++j) k_dma(tile_words(vk, j, kBC), j * kKTileBytes);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(vv, min(2, T - 1), kBC);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fetch_v_one(r, i);
-  }
 
   // ---- queries: qf[kk] = codes of dims 64 kk + 32 hi .. +32 of this
   // lane's query; c = softmax scale * log2 e * (q scale) * (k scale)
@@ -334,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
       const int kk = (step - 4) >> 1, kb = (step - 4) & 1;
       return lds_frag(lds + kf[kk][0] + (kslot_bytes + kb * 4096), lds + kf[kk][1] + (kslot_bytes + kb * 4096));
     }
-    return lds_frag(lds + vf[0] + (vslot_bytes + step * 2048), lds + vf[1] + (vslot_bytes + step * 2048));
+    return lds_read_tr8x4(lds + vtr[step] + vslot_bytes);
   };
   auto matrix_step = [&](int step, i32x8_t f) __attribute__((always_inline)) {
     if (step >= 4) {
@@ -440,29 +434,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   // Schedule and ring reuse as in the bf16 kernel: QK^T(0), vector
   // half-step of tile 0, then per tile j a matrix half-step (PV(j),
   // QK^T(j+1)) and the vector half-step of tile j+1; group 1 runs one
-  // barrier behind group 0.  Ring traffic of matrix half-step j: write V^T
-  // tile j+2, fetch V tile j+3 into VGPRs, copy K tile j+3 into LDS.  The
-  // V^T slot of tile j+2 last held tile j-2 (read by PV(j-2) in matrix
-  // half-step j-2) and the K slot of tile j+3 last held tile j-1 (read by
-  // QK^T(j-1) in matrix half-step j-2): at least one barrier separates
-  // those reads from either group's writes.  Fetch indices are clamped to
-  // T-1; extra copies land in slots no later step reads.  The vmcnt wait in
-  // each vector half-step retires the previous matrix half-step's loads.
-  constexpr int kStoreStep = 0, kVLoad0 = 1, kKLoadStep = 5;
+  // barrier behind group 0.  Ring traffic of matrix half-step j: copy V and
+  // K tile j+3 into LDS.  Both slots last held tile j-1 (read by PV(j-1) in
+  // matrix half-step j-1 and by QK^T(j-1) in matrix half-step j-2): at
+  // least one barrier separates those reads from either group's writes.
+  // Tile indices are clamped to T-1; extra copies land in slots no later
+  // step reads.  The vmcnt wait in each vector half-step retires the
+  // previous matrix half-step's copies.
+  constexpr int kVLoadStep = 1, kKLoadStep = 5;
   auto vector_tail = [&](int kslot_bytes, int vslot_bytes, i32x8_t *ring) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    prepare_v();
 #pragma unroll
     for (int i = 0; i < kPre; ++i) ring[i] = frag(i, kslot_bytes, vslot_bytes);
   };
   auto iteration = [&](int j, auto slot, i32x8_t *ring) __attribute__((always_inline)) {
     constexpr int R = decltype(slot)::value;
-    constexpr int kCur = R * kKTileBytes;                       // V^T slot of tile j (same offset in both rings)
+    constexpr int kCur = R * kKTileBytes;                       // V slot of tile j (same offset in both rings)
     constexpr int kNext = ((R + 1) % kSlots) * kKTileBytes;    // slots of tile j+1
-    constexpr int kPlus2 = ((R + 2) % kSlots) * kKTileBytes;   // V^T slot of tile j+2
-    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
+    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // slots of tile j+3
     const int tn = min(j + 3, T - 1);
-    const __amdgpu_buffer_rsrc_t rvn = tile_rsrc(vv, tn, kBC);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(3);
     __builtin_amdgcn_sched_barrier(0);
@@ -471,8 +461,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
       const i32x8_t f = ring[step % kPre];
       if (step + kPre < 8) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
-      if (step == kStoreStep) store_v(kPlus2);
-      if (step >= kVLoad0 && step < kVLoad0 + 4) fetch_v_one(rvn, step - kVLoad0);
+      if (step == kVLoadStep) v_dma(tile_words(vv, tn, kBC), kPlus3);
       if (step == kKLoadStep) k_dma(tile_words(vk, tn, kBC), kPlus3);
       __builtin_amdgcn_sched_barrier(0);
     }
