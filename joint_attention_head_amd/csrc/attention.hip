@@ -36,8 +36,10 @@
 //    no tile passes through VGPRs.  Buffer-resource loads return 0 past the
 //    end of a head, so ragged tails need no branches; the softmax masks
 //    keys >= N.
-//  * Online softmax in base 2: one FMA per score gives x = c*S - b (c =
-//    scale * log2 e, b = the row's running shift), then p = 2^x.  The row
+//  * Online softmax in base 2: x = c*S - b (c = scale * log2 e, b = the
+//    row's running shift), then p = 2^x.  The plain form spends one FMA per
+//    score on x; the fused form gets it from the MFMA, with c folded into
+//    the queries and -b as the accumulator's initial value.  The row
 //    maximum is only scanned when the tile's row sum (an upper bound of
 //    every probability in it) exceeds 2^16; b then moves up to the maximum
 //    if that exceeds it by more than 8, with O and l rescaled.  O / l is
@@ -94,9 +96,11 @@ __device__ __forceinline__ bf16x8_t lds_read_tr2(const char *p) {
 }
 
 // Queries of the fused entry points: raw Q -> RMSNorm over the 128 dims ->
-// rotation of each adjacent pair by its axis position times frequency ->
-// bf16 (the prologue's operations, on the 64 dims this lane holds:
-// 16 kk + 8 hi + i; the other 64 are in lane ^ 32).
+// rotation of each adjacent pair by its axis position times frequency
+// (the prologue's operations, on the 64 dims this lane holds:
+// 16 kk + 8 hi + i; the other 64 are in lane ^ 32) -> times c = softmax
+// scale * log2 e -> bf16, so that the QK^T MFMA yields base-2 logits.  The
+// one bf16 rounding of Q' is the same as the prologue's, applied to c Q'.
 __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const HeadView &vq, int q_row,
                                              int hi) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
@@ -137,8 +141,8 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
       pair_rotation(a, pos, 8 * kk + 4 * hi + m, sn, cs);
       const float u = x[2 * m] * w[2 * m] * rstd;
       const float v = x[2 * m + 1] * w[2 * m + 1] * rstd;
-      qf[kk][2 * m] = (__bf16)(u * cs - v * sn);
-      qf[kk][2 * m + 1] = (__bf16)(u * sn + v * cs);
+      qf[kk][2 * m] = (__bf16)((u * cs - v * sn) * a.scale_log2);
+      qf[kk][2 * m + 1] = (__bf16)((u * sn + v * cs) * a.scale_log2);
     }
   }
 }
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   f32x16_t s[2];
   bf16x8_t pf[4];
   float b_run = 0.f;      // this row's running shift, base-2 units
+  f32x16_t bias = {};     // fused: -b_run in every element
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
   const f32x16_t zero = {};
 
@@ -297,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   auto matrix_step = [&](int step, bf16x8_t f) __attribute__((always_inline)) {
     if (step >= 16) {
       const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : zero, 0, 0, 0);
+      // fused: Q' carries c and the accumulator starts at -b
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : (FUSEQ ? bias : zero), 0, 0, 0);
     } else {
       const int st = step >> 2, db = step & 3;
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
@@ -306,8 +312,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 
   // Online softmax of tile j.  Lane owns query l32 and keys
   // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]);
-  // one FMA per score turns S into x = c*S - b (c = softmax scale *
-  // log2 e).  Common case: p = 2^x straight away; the row maximum is
+  // x = c*S - b (c = softmax scale * log2 e) by one FMA per score, or
+  // straight from the MFMA in the fused form.  Common case: p = 2^x
+  // straight away; the row maximum is
   // only needed when some p may be large, which the tile's own row sum
   // (>= every p in it) tells.  Then, or on the first tile, b moves up to the
   // row maximum when that exceeds it by more than 8 (first tile: moves to
@@ -315,10 +322,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // always and O / l is unchanged.
   auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value != 0;
+    if constexpr (!FUSEQ) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
+        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
+    }
     if (j * kBC + kBC > N) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -367,6 +376,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       if (kFirst || __builtin_amdgcn_ballot_w64(mx > 8.0f) != 0) {
         const float d = kFirst ? mx : fmaxf(mx, 0.f);
         b_run += d;
+        if constexpr (FUSEQ) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bias[i] = -b_run;
+        }
         if constexpr (!kFirst) {
           const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
