@@ -21,8 +21,10 @@
 //  * P is stored as e4m3(p'), p' = 2^6 p relative to the row's running
 //    shift (a shift puts the row maximum at 2^6): every p' stays <= 448,
 //    the largest finite E4M3 value, and values down to p = 2^-12 keep the
-//    full 3-bit mantissa.  l sums the fp32 p'; O / l is unchanged by the
-//    factor.
+//    full 3-bit mantissa.  O / l is unchanged by the factor.
+//  * l sums the rounded P, the values PV multiplies, on the matrix cores:
+//    one 16 x 16 x 128 MFMA per tile against a constant ones operand (see
+//    `lsum`), so the softmax VALU does no additions.
 //  * Ping-pong: two groups of four waves, one wave of each group per SIMD;
 //    in every phase one group runs its matrix half-step (PV of the current
 //    tile, QK^T of the next: 8 MFMAs of 64 cycles, raised wave priority)
@@ -53,14 +55,12 @@ constexpr int kKTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes
 constexpr int kVTileBytes = kBC * kHeadDim;       // 8 KiB, row = key (128 codes)
 constexpr int kVRingOffset = kSlots * kKTileBytes;
 constexpr int kLdsBytes = kSlots * (kKTileBytes + kVTileBytes);  // 64 KiB
-// After a shift the row maximum is p' = 2^kPExp.  A tile whose lane sums of
-// p' are all <= kSumOk has every p' <= 448 and needs no maximum; otherwise
-// the shift moves when some p' exceeds 2^kShiftAt.  (A lower kPExp would
-// make the scan rarer still, but sends two more binades of small p' to
-// E4M3 subnormals.)
+// After a shift the row maximum is p' = 2^kPExp; the shift moves when some
+// p' of a tile would exceed 2^kShiftAt, so every p' stays <= 2^8 < 448.
+// (A lower kPExp would make shifts rarer, but sends two more binades of
+// small p' to E4M3 subnormals.)
 constexpr float kPExp = 6.f;
 constexpr float kShiftAt = 8.f;
-constexpr float kSumOk = 448.f;
 
 // LDS layouts.
 //  K tile : row = key (128 B = 8 chunks of 16 B); chunk c of key r sits at
@@ -98,6 +98,11 @@ __device__ __forceinline__ i32x8_t lds_frag(const char *p0, const char *p1) {
 // D = C + A B on E4M3 operands (unit block scales: exponent 127).
 __device__ __forceinline__ f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// D = C + A B, 16 x 16 x 128 on E4M3 operands (unit block scales).
+__device__ __forceinline__ f32x4_t mfma16_f8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 // D = C + 2^(sb - 127) A B: sb is this lane's E8M0 block scale of B, i.e.
 // of the 32 B elements the lane holds (its column, one half of k).
@@ -315,7 +320,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   i32x8_t pf;              // P^T operand: byte 16 kb + r = p' of s[kb][r]
   float b_run = 0.f;       // this row's running shift, base-2 units
   f32x16_t bias = {};      // fused: -b_run in every element
-  float l_part[2] = {0.f, 0.f};
+  // Row sums of the rounded P by the matrix cores: read as the B operand of
+  // a 16 x 16 x 128 MFMA, the P^T operand gives column l % 16, k-block
+  // l / 16 the bytes of query 16 ((l / 16) % 2) + l % 16 at k-slots
+  // 32 (l / 32) ..; an A operand of ones in k-blocks of the same parity as
+  // bit 2 of the row sums, in output row i, all 64 slots of query
+  // 16 ((i / 4) % 2) + column, and lane l holds rows 4 (l / 16) .. +3 of
+  // column l % 16: the sum of its own query, four times.
+  f32x4_t lsum = {};
+  i32x8_t lones;
+  {
+    const int v = (((lane >> 4) & 1) == ((lane >> 2) & 1)) ? 0x38383838 : 0;   // E4M3 1.0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lones[i] = v;
+  }
   const f32x16_t zero = {};
 
   // Matrix half-step as an 8-step software pipeline: steps 0..3 are PV of
@@ -345,10 +363,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
   // Online softmax of tile j (see the header comment): x = c*S - b by one
   // FMA per score (fused: by the MFMA's scale and accumulator), p' = 2^x.
-  // The row maximum is scanned only when some lane's sum of p' (>= each of
-  // them) exceeds kSumOk, and on the first tile; b moves so that the maximum
-  // lands at 2^kPExp when it passes 2^kShiftAt (first tile: always), with O
-  // and l rescaled.
+  // The lane maximum of x (16 max3) decides: when some lane's exceeds
+  // kShiftAt, and on the first tile, b moves so that the row maximum lands
+  // at 2^kPExp (first tile: always), with O and l rescaled.
   auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value != 0;
     if constexpr (!FUSEQ) {
@@ -366,69 +383,54 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
           if (key >= N) s[kb][r] = -INFINITY;
         }
     }
-    float t[2];
     auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float acc = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float e0 = __builtin_amdgcn_exp2f(s[kb][4 * u + 0]);
           const float e1 = __builtin_amdgcn_exp2f(s[kb][4 * u + 1]);
           const float e2 = __builtin_amdgcn_exp2f(s[kb][4 * u + 2]);
           const float e3 = __builtin_amdgcn_exp2f(s[kb][4 * u + 3]);
-          acc += (e0 + e1) + (e2 + e3);
           pf[4 * kb + u] = (int)f32x4_to_e4m3(e0, e1, e2, e3);
         }
-        t[kb] = acc;
-      }
     };
-    if constexpr (!kFirst) exps();
-    const float tot = t[0] + t[1];
-    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= kSumOk)) != 0) {
-      float mq[2];
+    // lane maximum of x - b (max3 chains)
+    float m = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float m = fmaxf(s[kb][0], s[kb][1]);
+    for (int r = 2; r < 16; ++r) m = fmaxf(m, s[0][r]);
 #pragma unroll
-        for (int r = 2; r < 16; ++r) m = fmaxf(m, s[kb][r]);
-        mq[kb] = m;
-      }
-      float mx = fmaxf(mq[0], mq[1]);
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, s[1][r]);
+    if (kFirst || __builtin_amdgcn_ballot_w64(m > kShiftAt) != 0) {
+      float mx = m;
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
         mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
       }
-      if (kFirst || __builtin_amdgcn_ballot_w64(mx > kShiftAt) != 0) {
-        // first tile: any shift (mx is finite: key 0 is in the tile)
-        const float d = kFirst ? mx - kPExp : fmaxf(mx - kPExp, 0.f);
-        b_run += d;
-        if constexpr (FUSEQ) {
+      // first tile: any shift (mx is finite: key 0 is in the tile)
+      const float d = kFirst ? mx - kPExp : fmaxf(mx - kPExp, 0.f);
+      b_run += d;
+      if constexpr (FUSEQ) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) bias[i] = -b_run;
-        }
-        if constexpr (!kFirst) {
-          const float alpha = __builtin_amdgcn_exp2f(-d);
-#pragma unroll
-          for (int g = 0; g < 2; ++g) l_part[g] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] -= d;
-        exps();
+        for (int i = 0; i < 16; ++i) bias[i] = -b_run;
       }
-    }
+      if constexpr (!kFirst) {
+        const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) l_part[g] += t[g];
+        for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= d;
+    }
+    exps();
     // keep the exponentials in this (vector) half-step
     asm volatile("" : "+v"(pf));
-#pragma unroll
-    for (int g = 0; g < 2; ++g) asm volatile("" : "+v"(l_part[g]));
   };
 
   // Schedule and ring reuse as in the bf16 kernel: QK^T(0), vector
@@ -461,6 +463,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
       const i32x8_t f = ring[step % kPre];
       if (step + kPre < 8) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
+      if (step == 3) lsum = mfma16_f8(lones, pf, lsum);   // row sums of P(j)
       if (step == kVLoadStep) v_dma(tile_words(vv, tn, kBC), kPlus3);
       if (step == kKLoadStep) k_dma(tile_words(vk, tn, kBC), kPlus3);
       __builtin_amdgcn_sched_barrier(0);
@@ -499,11 +502,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
   // ---- epilogue: O * s_v / l, one bf16 rounding; lane holds query l32 and
   // head dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end drop
-  float l_run = l_part[0] + l_part[1];
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
-    l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
-  }
+  const float l_run = lsum[0];   // all 64 keys of every tile, rounded P
   const float inv = o_scale / l_run;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
