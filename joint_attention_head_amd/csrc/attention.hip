@@ -342,13 +342,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int kb = st >> 1, r0 = 8 * (st & 1);
-        float acc = 0.f;
+        float acc;   // starts at the first pair: 0 + x is not folded (-0)
         bf16x8_t pv8;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           const float e0 = __builtin_amdgcn_exp2f(s[kb][r0 + i]);
           const float e1 = __builtin_amdgcn_exp2f(s[kb][r0 + i + 1]);
-          acc += e0 + e1;
+          acc = i ? acc + (e0 + e1) : e0 + e1;
           pv8[i] = (__bf16)e0;
           pv8[i + 1] = (__bf16)e1;
         }
