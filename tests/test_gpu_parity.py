@@ -218,6 +218,92 @@ def test_forward_bf16_logit_range_across_tiles(growth):
     assert rel < 1e-2
 
 
+def _tile_factors(N, growth, big):
+    """Per-key factors that change the logit scale from one 64-key tile to
+    the next (rising, falling: first tile dominates, spike: tile 4)."""
+    tiles = torch.arange(N) // 64
+    if growth == "rising":
+        return 1.0 + (big - 1.0) / 6.0 * tiles.float()
+    if growth == "falling":
+        return torch.where(tiles == 0, big, 1.0)
+    return torch.where(tiles == 4, big, 1.0)
+
+
+def _q_prime(q, w_q, pos):
+    """The queries' RMSNorm + RoPE, as the fused kernels apply them."""
+    return oracle.rope(oracle.rms_norm(q, w_q.double().numpy(), 1e-6), pos.numpy())
+
+
+LOG2E_OVER_SQRT_D = math.log2(math.e) / math.sqrt(128)
+
+
+def _q_rounded_bf16(qp):
+    """Q' as the fused bf16 kernel holds it: c Q' rounded once to bf16
+    (c = log2 e / sqrt(d)), divided back by c in fp64."""
+    c = LOG2E_OVER_SQRT_D
+    return torch.from_numpy(qp * c).to(torch.bfloat16).double().numpy() / c
+
+
+def _q_rounded_e4m3(qp, k_scale):
+    """Q' as the fused fp8 kernel encodes it: per query, codes of Q' g / 2^e
+    with g = c * (k scale) and e = ceil(log2(amax g / 448)), so that the
+    largest code lies in (224, 448]; returned as codes * 2^e / g."""
+    g = LOG2E_OVER_SQRT_D * k_scale.double().numpy()[:, :, None, None]
+    amax = np.abs(qp).max(axis=-1, keepdims=True)
+    e = np.ceil(np.log2(amax * g / 448.0))
+    codes = torch.from_numpy(qp * g / 2.0 ** e).to(torch.float8_e4m3fn).double().numpy()
+    return codes * 2.0 ** e / g
+
+
+@pytest.mark.parametrize("growth", ["rising", "falling", "spike"])
+def test_forward_fused_bf16_logit_range_across_tiles(growth):
+    """The running shift of the fused kernel (whose QK^T accumulators start
+    at -b) moving by tens of log2 units between key tiles.  At logits this
+    large the one bf16 rounding of c Q' alone moves the weights by more
+    than the tolerance, so the reference takes that rounding (of the
+    oracle's Q') as its input."""
+    inp = small(1, 2, 37, (20, 20))          # N = 437: 7 key tiles, ragged
+    N = inp.q.shape[2]
+    f = _tile_factors(N, growth, {"rising": 7.0, "falling": 6.0, "spike": 9.0}[growth])
+    k = (inp.k.float() * f[None, None, :, None]).to(torch.bfloat16)
+    o = fa.fluxattn_forward_fused_bf16(dev(inp.q), dev(k), dev(inp.v), dev(inp.w_q), dev(inp.pos))
+    torch.cuda.synchronize()
+    qr = _q_rounded_bf16(_q_prime(f64(inp.q), inp.w_q, inp.pos))
+    ref = oracle.attention(qr, f64(k), f64(inp.v))
+    rel = check_close(f64(o), ref, BF16_TOL, f"fused logit range {growth}")
+    assert rel < 1e-2
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("growth", ["rising", "falling", "spike"])
+def test_forward_fp8_logit_range_across_tiles(growth, fused):
+    """The fp8 kernel's running shift (lane maximum test, rescale of O and of
+    the matrix-core row sums) across tiles whose logit scale changes.  The
+    factors are milder than in bf16: E4M3 keys carry a 2^-4 relative
+    rounding, which at logits of tens of log2 units moves the softmax
+    weights themselves; here the largest logits are about 15.  The fused
+    form's reference takes the E4M3 re-encoding of the oracle's Q' (the
+    per-query scale rule) as its input, for the same reason."""
+    inp = small(1, 2, 37, (20, 20), None, "fp8", seed=3)
+    N = inp.q.shape[2]
+    f = _tile_factors(N, growth, 2.5)
+    k_real = torch.from_numpy(f64(inp.k, inp.k_scale)).float() * f[None, None, :, None]
+    amax = k_real.abs().amax(dim=(2, 3))
+    sk = (amax / 448.0).contiguous()
+    k8 = (k_real / sk[:, :, None, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    args = (dev(inp.q), dev(k8), dev(inp.v), dev(inp.q_scale), dev(sk), dev(inp.v_scale))
+    if fused:
+        o = fa.fluxattn_forward_fused_fp8(*args, dev(inp.w_q), dev(inp.pos))
+        qr = _q_rounded_e4m3(_q_prime(f64(inp.q, inp.q_scale), inp.w_q, inp.pos), sk)
+    else:
+        o = fa.fluxattn_forward_fp8(*args)
+        qr = f64(inp.q, inp.q_scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(qr, f64(k8, sk), f64(inp.v, inp.v_scale))
+    rel = check_close(f64(o), ref, FP8_TOL, f"fp8 {'fused ' if fused else ''}logit range {growth}")
+    assert rel < 1e-1
+
+
 def test_forward_bf16_invariants():
     inp = small(1, 2, 13, (10, 10))
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
