@@ -95,14 +95,18 @@ __device__ __forceinline__ i32x8_t lds_frag(const char *p0, const char *p1) {
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// D = C + A B on E4M3 operands (unit block scales: exponent 127).
+// D = C + A B on E4M3 operands.  Zero scale operands select the plain
+// v_mfma_f32_32x32x64_f8f6f4 (unit scales).  The scaled encoding, even with
+// unit scales, holds up the other wave's VALU while it runs: the softmax of
+// the other ping-pong group then stretches by the length of this group's
+// matrix half-step.
 __device__ __forceinline__ f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// D = C + A B, 16 x 16 x 128 on E4M3 operands (unit block scales).
+// D = C + A B, 16 x 16 x 128 on E4M3 operands (plain encoding, unit scales).
 __device__ __forceinline__ f32x4_t mfma16_f8(i32x8_t a, i32x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 // D = C + 2^(sb - 127) A B: sb is this lane's E8M0 block scale of B, i.e.
 // of the 32 B elements the lane holds (its column, one half of k).
