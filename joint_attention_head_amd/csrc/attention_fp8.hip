@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   f32x16_t s[2];
-  i32x8_t pf;              // P^T operand: byte 16 kb + r = p' of s[kb][r]
+  i32x8_t pf = {};         // P^T operand: byte 16 kb + r = p' of s[kb][r]
   float b_run = 0.f;       // this row's running shift, base-2 units
   f32x16_t bias = {};      // fused: -b_run in every element
   // Row sums of the rounded P by the matrix cores: read as the B operand of
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
           const float e1 = __builtin_amdgcn_exp2f(s[kb][4 * u + 1]);
           const float e2 = __builtin_amdgcn_exp2f(s[kb][4 * u + 2]);
           const float e3 = __builtin_amdgcn_exp2f(s[kb][4 * u + 3]);
-          pf[4 * kb + u] = (int)f32x4_to_e4m3(e0, e1, e2, e3);
+          pf[4 * kb + u] = (int)f32x4_to_e4m3_over(e0, e1, e2, e3, pf[4 * kb + u]);
         }
     };
     // lane maximum of x - b (max3 chains)

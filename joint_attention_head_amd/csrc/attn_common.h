@@ -58,6 +58,14 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+// The same into a register whose old contents are dead: the first convert
+// writes only the low half, so passing the old word (instead of 0) spares
+// the v_mov that would clear the high half; the second convert overwrites it.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_over(float a, float b, float c, float d, int old) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
