@@ -176,6 +176,11 @@ fluxattn_status fluxattn_forward_bf16(
  * Q = e4m3(q)*q_scale[b,h], and likewise K and V.  Output o is bf16
  * [B,H,N,D] and must not overlap q, k or v.  (blog post above, section
  * "Quantized and sparse attention": FP8 for both the QK and the V operands.)
+ * Q K^T and P.V run on the fp8 matrix cores with fp32 accumulation; P is
+ * encoded as E4M3 of 2^6 p relative to a running shift of each row (so every
+ * code stays <= 2^8); the normaliser sums those E4M3 values, the ones P.V
+ * multiplies; O is divided by it, times v_scale, and rounded once to bf16.
+ * Deterministic.
  */
 fluxattn_status fluxattn_forward_fp8(
     const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -195,8 +200,9 @@ fluxattn_status fluxattn_forward_fp8(
  *   q_norm_w  fp32 [D] query RMSNorm weights, 16-byte aligned.
  *   pos_ids, axes_*, theta, eps  as in fluxattn_qk_norm_rope_bf16.
  *   softmax_scale  as in fluxattn_forward_bf16.
- * Q' is computed in fp32 and rounded to bf16 once, as the prologue would
- * store it.  The rotation frequencies are 2^(j * -2 log2(theta) / axes_a)
+ * Q' is computed in fp32, multiplied by c = softmax scale * log2 e and
+ * rounded to bf16 once (the prologue rounds Q' itself once), so the QK^T
+ * product yields base-2 logits directly.  The rotation frequencies are 2^(j * -2 log2(theta) / axes_a)
  * evaluated on the device (within 1e-6 relative of the host table the
  * prologue uses) and the angles go through the hardware sine / cosine
  * after reduction to one revolution (absolute error about
@@ -211,8 +217,11 @@ fluxattn_status fluxattn_forward_fused_bf16(
 
 /*
  * fp8 form: E4M3 q (raw), k (prepared), v with fp32 [B,H] scales; the
- * queries are dequantised, normalised and rotated in fp32 and kept in
- * bf16.  Output bf16.
+ * queries are dequantised, normalised and rotated in fp32, then re-encoded
+ * in E4M3 per query: codes of Q' * g / 2^e with g = softmax scale * log2 e *
+ * k_scale and e the smallest integer keeping every code within 448; the
+ * QK^T product applies 2^e as its block scale.  Numerics otherwise as
+ * fluxattn_forward_fp8.  Output bf16.
  */
 fluxattn_status fluxattn_forward_fused_fp8(
     const uint8_t *q, const uint8_t *k, const uint8_t *v,
