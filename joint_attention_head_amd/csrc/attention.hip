@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     constexpr int R = decltype(slot)::value;
     constexpr int kCur = R * kKTileBytes;                       // V slot of tile j (same byte offset in both rings)
     constexpr int kNext = ((R + 1) % kSlots) * kKTileBytes;    // slots of tile j+1
-    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // K slot of tile j+3
+    constexpr int kPlus3 = ((R + 3) % kSlots) * kKTileBytes;   // slots of tile j+3 (K and V)
     const int tn = min(j + 3, T - 1);
     // the vector half-step wrote no LDS, and the fragment reads it issued
     // touch a slot no wave writes before the next barrier: a plain barrier

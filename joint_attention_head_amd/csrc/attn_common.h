@@ -32,26 +32,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Four E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value).
-__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2_t r;
-  r[0] = pack_bf16(lo[0], lo[1]);
-  r[1] = pack_bf16(hi[0], hi[1]);
-  return r;
-}
-
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(u32x2_t w) {
-  const u32x2_t a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-  u32x4_t v;
-  v[0] = a[0];
-  v[1] = a[1];
-  v[2] = b[0];
-  v[3] = b[1];
-  return v;
-}
-
 // Four fp32 -> four E4M3 codes (round to nearest even), byte i = value i.
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -132,13 +112,10 @@ __device__ __forceinline__ HeadView head_view(const void *p, const Strides &st, 
   return v;
 }
 
-// Buffer descriptor of key tile t (tile_keys rows) of a head: base moved
-// to the tile, records cut to what is left of the head, so lane offsets
-// stay tile-independent.  Scalar arithmetic only.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const HeadView &v, int t, int tile_keys) {
-  const uint32_t skip = (uint32_t)t * (uint32_t)tile_keys * v.row;
-  return make_rsrc(v.base + skip, v.bytes - skip);
-}
+// Buffer descriptor words of key tile t (tile_keys rows) of a head, for the
+// direct global -> LDS copies: base moved to the tile, records cut to what
+// is left of the head, so lane offsets stay tile-independent.  Scalar
+// arithmetic only.
 __device__ __forceinline__ i32x4_t tile_words(const HeadView &v, int t, int tile_keys) {
   const uint32_t skip = (uint32_t)t * (uint32_t)tile_keys * v.row;
   return rsrc_words(v.base + skip, v.bytes - skip);
