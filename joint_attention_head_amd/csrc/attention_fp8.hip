@@ -448,11 +448,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   // step reads.  The vmcnt wait in each vector half-step retires the
   // previous matrix half-step's copies.
   constexpr int kVLoadStep = 1, kKLoadStep = 5;
-  auto vector_tail = [&](int kslot_bytes, int vslot_bytes, i32x8_t *ring) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // First kPre fragments of the next matrix half-step (V slot of tile j+1,
+  // K slot of tile j+2), requested at the start of the vector half-step so
+  // the LDS reads overlap the softmax.  Both tiles are complete: they were
+  // copied in matrix half-steps j-2 and j-1, and every wave has retired its
+  // part and passed a barrier since.  The only slots written before the
+  // next barrier are those of tile j+3.
+  auto prefetch = [&](int kslot_bytes, int vslot_bytes, i32x8_t *ring) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) ring[i] = frag(i, kslot_bytes, vslot_bytes);
   };
+  // end of the vector half-step: retire this wave's copies of the matrix
+  // half-step just done, before the next barrier
+  auto vector_tail = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto iteration = [&](int j, auto slot, i32x8_t *ring) __attribute__((always_inline)) {
     constexpr int R = decltype(slot)::value;
     constexpr int kCur = R * kKTileBytes;                       // V slot of tile j (same offset in both rings)
@@ -478,8 +486,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
     asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     __syncthreads();
     if (j + 1 < T) {
+      prefetch(((R + 2) % kSlots) * kKTileBytes, kNext, ring);
       softmax(j + 1, Slot<0>{});
-      vector_tail(((R + 2) % kSlots) * kKTileBytes, kNext, ring);
+      vector_tail();
     }
   };
 
@@ -489,8 +498,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   for (int step = 4; step < 8; ++step) matrix_step(step, frag(step, 0, 0));
   __syncthreads();
   i32x8_t ring[kPre];
+  prefetch(1 * kKTileBytes, 0, ring);
   softmax(0, Slot<1>{});
-  vector_tail(1 * kKTileBytes, 0, ring);
+  vector_tail();
   int j = 0;
   for (; j + kSlots <= T; j += kSlots) {
     iteration(j, Slot<0>{}, ring);
