@@ -16,8 +16,12 @@ attention kernel's roofline fraction (its own average launch time from HIP
 events on the launch stream), the same figures at N=4608 (FLUX-dev 1024x1024)
 under "also", the fp8 path (E4M3 Q/K/V, fp8 matrix cores) on the 2048x2048
 image-to-image workload (B=1, H=24, N = 512 + 2 x 128x128 = 33280) under
-"fp8" with its roofline against the fp8 MFMA peak, and the fp64 CPU oracle
-timed on a bounded sample of the main workload under "cpu_baseline".
+"fp8" with its roofline against the fp8 MFMA peak, every workload's forward
+TFLOP/s and MFMA fraction under "all_configs", and the fp64 CPU oracle timed
+on a bounded sample of the main workload under "cpu_baseline".  Each roofline
+also carries the MFMA-busy fraction and sustained clock of its kernel from
+the committed rocprofv3 counter summary ("counters", null once the kernel
+source has changed since it was taken).
 """
 from __future__ import annotations
 
@@ -25,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -74,6 +79,37 @@ def measured_traffic(path: str, kind: str = "bf16"):
         return None
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_mfma_valu_counters.txt")
+COUNTER_KERNEL = {"bf16": "attn_fwd_kernel", "fp8": "attn_fwd_fp8_kernel"}
+
+
+def measured_mfma_busy(kind: str = "bf16"):
+    """MFMA-busy fraction and sustained clock of one attention kernel from the
+    committed rocprofv3 counter summary, or None if that kernel's source
+    changed since the counters were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    hashes, block, cur = {}, {}, None
+    with open(COUNTERS) as f:
+        for line in f:
+            m = re.search(r"bf16 sha256_16 ([0-9a-f]+), fp8 sha256_16 ([0-9a-f]+)", line)
+            if m:
+                hashes = {"bf16": m.group(1), "fp8": m.group(2)}
+            elif line.startswith("kernel:"):
+                cur = line.split(":", 1)[1].strip()
+                block[cur] = {}
+            elif cur and ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                block[cur][k.strip()] = v.strip()
+    vals = block.get(COUNTER_KERNEL[kind], {})
+    if hashes.get(kind) != kernel_source_hash(kind):
+        return None
+    try:
+        return {"mfma_busy_fraction": float(vals["mfma_busy_fraction"]), "clock_GHz": float(vals["clock_GHz"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -83,6 +119,8 @@ def parse():
     p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
     p.add_argument("--fp8", default="i2i_2048", help="fp8 workload ('' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-all-configs", dest="all_configs", action="store_false",
+                   help="skip the per-workload table (every workload's forward TFLOP/s and MFMA fraction)")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--path", choices=("fused", "unfused"), default="fused")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -236,10 +274,12 @@ def main():
         sys.exit(2)
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     main_res = run_gpu(args.workload, args.steps, args.warmup, args.path)
+    done = {args.workload: main_res}
     print(f"bench: {args.workload} forward {main_res['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
     also = None
     if args.also:
         r = run_gpu(args.also, args.steps, args.warmup, args.path)
+        done[args.also] = r
         w = r["workload"]
         also = {
             "workload": f"{w.name}: B={w.B} H={w.H} N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128 bf16",
@@ -253,6 +293,7 @@ def main():
     fp8 = None
     if args.fp8:
         r = run_gpu(args.fp8, args.steps, args.warmup, args.path)
+        done[args.fp8] = r
         w = r["workload"]
         fp8 = {
             "workload": f"{w.name}: 2048x2048 image-to-image, B={w.B} H={w.H} "
@@ -272,10 +313,30 @@ def main():
                 "frac": round(r["forward_tflops"] / FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(args.path, "fp8"),
                 "launch_ms": round(r["forward_ms"], 4),
+                "counters": measured_mfma_busy("fp8") if args.path == "fused" else None,
             },
             "prologue_gbs": round(r["prologue_gbs"], 1),
         }
         print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+    all_configs = None
+    if args.all_configs:
+        from workloads import WORKLOADS
+        all_configs = {}
+        for name in WORKLOADS:
+            r = done.get(name)
+            if r is None:
+                r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path)
+            w = r["workload"]
+            peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
+            all_configs[name] = {
+                "B": w.B, "H": w.H, "N": w.N, "dtype": w.dtype,
+                "value": round(r["value"], 2),
+                "forward_ms": round(r["forward_ms"], 4),
+                "forward_tflops": round(r["forward_tflops"], 2),
+                "frac": round(r["forward_tflops"] / peak, 4),
+                "prologue_gbs": round(r["prologue_gbs"], 1),
+            }
+            print(f"bench: {name} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
     if args.calibrate_copy:
         calibrate_copy()
     cpu = None
@@ -313,6 +374,7 @@ def main():
             "frac": round(main_res["forward_tflops"] / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
             "launch_ms": round(main_res["forward_ms"], 4),
+            "counters": measured_mfma_busy("bf16") if args.path == "fused" else None,
         },
         "prologue": {
             "kernel": "prologue_bf16_kernel (%s)" % ("keys only" if args.path == "fused" else "queries and keys"),
@@ -325,6 +387,7 @@ def main():
         },
         "also": also,
         "fp8": fp8,
+        "all_configs": all_configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
