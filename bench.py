@@ -123,6 +123,9 @@ def parse():
                    help="skip the per-workload table (every workload's forward TFLOP/s and MFMA fraction)")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--path", choices=("fused", "unfused"), default="fused")
+    p.add_argument("--groups", type=int, default=0,
+                   help="attention workgroup setting: 0 = one per compute unit, key ranges split where that "
+                        "balances the last round (default); < 0 = never split; > 0 = that many workgroups")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
@@ -272,7 +275,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
-    print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    import joint_attention_head_amd as fa
+    fa.fluxattn_set_forward_groups(args.groups)
+    print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} groups={args.groups}",
+          file=sys.stderr, flush=True)
     main_res = run_gpu(args.workload, args.steps, args.warmup, args.path)
     done = {args.workload: main_res}
     print(f"bench: {args.workload} forward {main_res['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
@@ -363,6 +369,7 @@ def main():
             "workload": f"{w.name}: 2048x2048 text-to-image with CFG, B={w.B} H={w.H} "
                         f"N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128, prologue + attention",
             "path": args.path,
+            "groups": args.groups,
             "B": w.B, "H": w.H, "N": w.N, "head_dim": 128,
         },
         "roofline": {

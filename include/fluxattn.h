@@ -337,6 +337,34 @@ const char *fluxattn_status_string(fluxattn_status s);
 /* hipError_t of this thread's most recent FLUXATTN_ERR_HIP (0 if none). */
 int fluxattn_last_hip_error(void);
 
+/*
+ * Execution setting of every attention launch (forward, fused and joint
+ * entry points); the function computed is the one described above.  A
+ * launch normally runs one workgroup per 256-query block of each (b,h).
+ * When the blocks outnumber G workgroups the grid can instead be G
+ * persistent workgroups, each taking an equal contiguous share of the
+ * (query block, 64-key tile) pairs in (b, h, query block, key tile) order,
+ * so that the last round of blocks no longer leaves compute units idle.
+ * A block whose keys fall in two shares is computed in two pieces; each
+ * piece leaves its fp32 partial O, row shift and normaliser in a
+ * workspace, and the piece finishing second merges the two and stores O.
+ * Results then differ from the uncut launch by fp32 summation order only.
+ *   groups == 0  (default) G = the device's compute units; cut only when
+ *                whole blocks would leave more than 3% of the last round
+ *                idle.
+ *   groups > 0   G = groups, cut whenever there are more blocks than G.
+ *   groups < 0   never cut.
+ * Process-wide, for launches made after the call.  A cut launch uses a
+ * workspace per (device, stream), allocated with hipMalloc by the first
+ * such launch on that stream (about 264 KiB per workgroup) and held until
+ * the process ends; launches on one stream share it in stream order.
+ * Returns FLUXATTN_ERR_INVALID_SHAPE for groups > 16384 (setting unchanged).
+ */
+fluxattn_status fluxattn_set_forward_groups(int32_t groups);
+
+/* The current setting of fluxattn_set_forward_groups. */
+int32_t fluxattn_get_forward_groups(void);
+
 /* Library version as 10000*major + 100*minor + patch. */
 int fluxattn_version(void);
 

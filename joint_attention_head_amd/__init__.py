@@ -63,6 +63,8 @@ EXPORTS = (
     "fluxattn_joint_attention_ex_fp8",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
+    "fluxattn_set_forward_groups",
+    "fluxattn_get_forward_groups",
     "fluxattn_version",
 )
 
@@ -121,6 +123,8 @@ _SIGS = {
                                          _i64, _i32, _i32, _i32, _f, _f, _f, _p],
     "fluxattn_joint_attention_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _p, _p, _L, _p, _p, _S, _p,
                                         _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _p],
+    "fluxattn_set_forward_groups": [_i32],
+    "fluxattn_get_forward_groups": [],
 }
 
 
@@ -380,6 +384,17 @@ def fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos
 
 
 # ---- strided views and token streams
+
+
+def fluxattn_set_forward_groups(groups: int):
+    """Workgroup count G of the attention launches: 0 = one per compute unit
+    with key-range splits only where they balance the last round, > 0 = G
+    (split whenever query blocks outnumber G), < 0 = never split."""
+    _check(lib().fluxattn_set_forward_groups(int(groups)))
+
+
+def fluxattn_get_forward_groups() -> int:
+    return int(lib().fluxattn_get_forward_groups())
 
 
 def layout_of(t: torch.Tensor) -> Layout:

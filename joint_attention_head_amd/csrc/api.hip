@@ -6,6 +6,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "fluxattn.h"
 #include "fluxattn_internal.h"
@@ -150,6 +153,101 @@ bool disjoint(const View &a, const View &b, int64_t B, int64_t H, int64_t N, int
   if (B > 1 && a.sb % a.sn) return false;
   const int64_t r = ((delta % a.sn) + a.sn) % a.sn;
   return r >= foot && r + foot <= a.sn;
+}
+
+// ---- key-range split of the forward launches
+
+// 0: one workgroup per compute unit, split when there are at least two
+// rounds of query blocks and whole blocks would leave more than 3% of the
+// last round idle; > 0: that many workgroups, split whenever there are more
+// query blocks; < 0: never.
+std::atomic<int32_t> g_forward_groups{0};
+constexpr int32_t kMaxGroups = 1 << 14;
+
+int32_t compute_units(int dev) {
+  static std::atomic<int32_t> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const int32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Split workspace of one (device, stream): arrival counts (zeroed once at
+// allocation; every launch leaves them at zero) then the partial results.
+// Launches on one stream run in order, so they share it safely; each other
+// stream gets its own.  Held until the process ends.
+struct Workspace {
+  void *p = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t split_count_bytes(int32_t groups) { return (static_cast<size_t>(groups) * 4 + 255) & ~size_t(255); }
+size_t split_bytes(int32_t groups) {
+  return split_count_bytes(groups) + static_cast<size_t>(groups) * 2 * kSplitPieceFloats * sizeof(float);
+}
+
+hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace &w = g_ws[std::make_pair(dev, s)];
+  if (w.bytes < bytes) {
+    if (w.p) {
+      hipError_t e = hipStreamSynchronize(s);   // earlier launches on s may still use it
+      if (e != hipSuccess) return e;
+      e = hipFree(w.p);
+      w.p = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return e;
+    }
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    e = hipMemset(p, 0, bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return e;
+    }
+    w.p = p;
+    w.bytes = bytes;
+  }
+  *out = w.p;
+  return hipSuccess;
+}
+
+// Fill a.split_* for a forward launch over nb query blocks of key_tiles
+// tiles each (split_groups stays 0 when the launch is not split).
+hipError_t plan_split(ForwardArgs &a, int64_t nb, hipStream_t s) {
+  a.split_groups = 0;
+  const int32_t setting = g_forward_groups.load(std::memory_order_relaxed);
+  if (setting < 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int32_t groups = setting > 0 ? setting : compute_units(dev);
+  if (groups < 2 || nb <= groups) return hipSuccess;
+  if (setting == 0) {
+    // default: only where whole rounds precede the tail (with fewer blocks
+    // the shares would desynchronise all key streaming) and the last round
+    // of whole blocks would leave more than 3% of the compute units idle
+    if (nb < 2 * static_cast<int64_t>(groups)) return hipSuccess;
+    const int64_t rounds = (nb + groups - 1) / groups;
+    if (nb * 100 >= rounds * groups * 97) return hipSuccess;
+  }
+  void *p = nullptr;
+  e = workspace_for(dev, s, split_bytes(groups), &p);
+  if (e != hipSuccess) return e;
+  a.split_cnt = static_cast<int32_t *>(p);
+  a.split_part = reinterpret_cast<float *>(static_cast<char *>(p) + split_count_bytes(groups));
+  a.split_groups = groups;
+  return hipSuccess;
 }
 
 // gfx950 check, cached per device (arch never changes for a device id).
@@ -355,6 +453,8 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
   }
   const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
                          is_contiguous(o, H, N, D));
+  const hipError_t ps = plan_split(a, forward_grid_blocks(BH, N), static_cast<hipStream_t>(stream));
+  if (ps != hipSuccess) return hip_fail(ps);
   const hipError_t e = FP8 ? launch_forward_fp8(a, fused, strided, static_cast<hipStream_t>(stream))
                            : launch_forward_bf16(a, fused, strided, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
@@ -593,6 +693,14 @@ const char *fluxattn_status_string(fluxattn_status s) {
 
 int fluxattn_last_hip_error(void) { return g_last_hip_error; }
 
-int fluxattn_version(void) { return 120; }
+fluxattn_status fluxattn_set_forward_groups(int32_t groups) {
+  if (groups > kMaxGroups) return FLUXATTN_ERR_INVALID_SHAPE;
+  g_forward_groups.store(groups, std::memory_order_relaxed);
+  return FLUXATTN_OK;
+}
+
+int32_t fluxattn_get_forward_groups(void) { return g_forward_groups.load(std::memory_order_relaxed); }
+
+int fluxattn_version(void) { return 130; }
 
 }  // extern "C"

@@ -58,6 +58,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+static_assert(kThreads == kSplitThreads, "split partials are laid out per thread of a 512-thread workgroup");
 constexpr int kBR = kWaves * 32;                  // query rows per workgroup
 constexpr int kBC = 64;                           // keys per tile
 constexpr int kSlots = 4;                         // per ring (K and V)
@@ -147,26 +148,20 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
   }
 }
 
+// Attention of one query block over key tiles [job.kt0, job.kt0 + job.T):
+// the whole head (job.cut < 0: O is stored) or one piece of a split block.
 template <bool FUSEQ, bool STRIDED>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int simd_of_wave[kWaves];
-
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *split_ticket, const SplitJob &job,
+                                         const int tid_in, const int group, const int gw) {
+  // lane constants are computed per job (an opaque copy of the thread id
+  // keeps them from being hoisted out of the job loop, where they would
+  // overlap the fused query transform's temporaries)
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
-
-  // ---- ping-pong groups: the two waves of a SIMD land in different groups
-  const int order = pingpong_order(simd_of_wave, wave, lane);
-  const int group = order & 1;
-  const int gw = order >> 1;                   // wave index inside the group
   const int rank = gw * 64 + lane;             // 0..255 inside the group
-
-  // ---- blockIdx -> (b*h, query tile), consecutive tiles per XCD
-  const int ntiles = (N + kBR - 1) / kBR;
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int bh = logical / ntiles;
-  const int qt = logical - bh * ntiles;
+  const int bh = job.bh, qt = job.qt, kt0 = job.kt0, T = job.T;
 
   // ---- per-head base pointers, token-row pitches and buffer extents
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 2, bh, a.H, N);
@@ -190,7 +185,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   const HeadView vo = head_view<STRIDED>(a.o, a.so, 2, bh, a.H, N);
 
   const float c = a.scale_log2;
-  const int T = (N + kBC - 1) / kBC;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
@@ -238,33 +232,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   // ---- ring traffic helpers
   // one of the two direct K copies of this wave: 1 KiB = 4 rows
   auto k_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
-    const uint32_t m0 = k_m0 + slot_bytes + 1024u * (uint32_t)i;
+    // the LDS address is added up here, not by the compiler: precomputed
+    // sums for every slot would hold 16 scalar registers through the loop
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_add_u32 m0, %0, %3\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(m0), "v"(k_dgoff[i]), "s"(words)
-        : "memory");
+        : "s"(k_m0), "v"(k_dgoff[i]), "s"(words), "s"(slot_bytes + 1024u * (uint32_t)i)
+        : "memory", "scc");
   };
   // one of the two direct V copies of this wave
   auto v_dma_one = [&](const i32x4_t &words, uint32_t slot_bytes, int i) __attribute__((always_inline)) {
-    const uint32_t m0 = k_m0 + kVRingOffset + slot_bytes + 1024u * (uint32_t)i;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_add_u32 m0, %0, %3\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(m0), "v"(v_dgoff[i]), "s"(words)
-        : "memory");
+        : "s"(k_m0), "v"(v_dgoff[i]), "s"(words), "s"(kVRingOffset + slot_bytes + 1024u * (uint32_t)i)
+        : "memory", "scc");
   };
 
   // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
   for (int j = 0; j < 3 && j < T; ++j) {
-    const i32x4_t w = tile_words(vk, j, kBC);
+    const i32x4_t w = tile_words(vk, kt0 + j, kBC);
     k_dma_one(w, j * kKTileBytes, 0);
     k_dma_one(w, j * kKTileBytes, 1);
-    const i32x4_t wv = tile_words(vv, j, kBC);
+    const i32x4_t wv = tile_words(vv, kt0 + j, kBC);
     v_dma_one(wv, j * kKTileBytes, 0);
     v_dma_one(wv, j * kKTileBytes, 1);
   }
@@ -328,12 +322,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
     }
-    if (j * kBC + kBC > N) {
+    if ((kt0 + j) * kBC + kBC > N) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int key = (kt0 + j) * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
           if (key >= N) s[kb][r] = -INFINITY;
         }
     }
@@ -448,8 +442,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
       const bf16x8_t f = ring[step % kPre];
       if (step + kPre < 32) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
-      if (step == kVLoad0 || step == kVLoad0 + kVLoadGap) v_dma_one(tile_words(vv, tn, kBC), kPlus3, step == kVLoad0 ? 0 : 1);
-      if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) k_dma_one(tile_words(vk, tn, kBC), kPlus3, step == kKLoad0 ? 0 : 1);
+      if (step == kVLoad0 || step == kVLoad0 + kVLoadGap) v_dma_one(tile_words(vv, kt0 + tn, kBC), kPlus3, step == kVLoad0 ? 0 : 1);
+      if (step == kKLoad0 || step == kKLoad0 + kKLoadGap) k_dma_one(tile_words(vk, kt0 + tn, kBC), kPlus3, step == kKLoad0 ? 0 : 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -489,6 +483,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
     l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
   }
+  // a piece of a split block: the piece that finishes second merges
+  if (job.cut >= 0 && !split_merge(a, job, o, b_run, l_run, tid, split_ticket)) return;
   const float inv = 1.0f / l_run;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
@@ -504,9 +500,39 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 }
 
 template <bool FUSEQ, bool STRIDED>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int simd_of_wave[kWaves];
+  __shared__ int split_ticket;
+
+  const int tid = threadIdx.x;
+  // ---- ping-pong groups: the two waves of a SIMD land in different groups
+  const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
+  const int group = order & 1;
+  const int gw = order >> 1;                   // wave index inside the group
+
+  // ---- this workgroup's share of the (query block, key tile) pairs; the
+  // range state waits in LDS (one copy per wave) while a job runs, so it
+  // takes no scalar registers there
+  __shared__ SplitRange range_lds[kWaves];
+  SplitRange *rs = &range_lds[tid >> 6];
+  {
+    const SplitRange r = split_range(a, kBR, kBC, xcd_logical_block(blockIdx.x, gridDim.x));
+    if ((tid & 63) == 0) *rs = r;
+  }
+  for (;;) {
+    SplitRange r = split_range_load(rs);
+    SplitJob job;
+    if (!split_next(r, job)) break;
+    if ((tid & 63) == 0) *rs = r;
+    attn_job<FUSEQ, STRIDED>(a, lds, &split_ticket, job, tid, group, gw);
+  }
+}
+
+template <bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.N + kBR - 1) / kBR;
-  const int64_t grid = ntiles * a.BH;
+  const int64_t grid = a.split_groups > 0 ? a.split_groups : ntiles * a.BH;
   // Raise the dynamic-LDS limit once per device (idempotent, so a race
   // between threads only repeats the call).
   static std::atomic<uint64_t> attr_done{0};
@@ -537,5 +563,6 @@ hipError_t launch_forward_bf16(const ForwardArgs &a, bool fused, bool strided, h
 }
 
 int64_t forward_grid_blocks(int64_t BH, int64_t N) { return BH * ((N + kBR - 1) / kBR); }
+int64_t forward_key_tiles(int64_t N) { return (N + kBC - 1) / kBC; }
 
 }  // namespace fluxattn

@@ -48,6 +48,7 @@ using namespace attn;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+static_assert(kThreads == kSplitThreads, "split partials are laid out per thread of a 512-thread workgroup");
 constexpr int kBR = kWaves * 32;                  // query rows per workgroup
 constexpr int kBC = 64;                           // keys per tile
 constexpr int kSlots = 4;                         // per ring (K and V)
@@ -202,31 +203,26 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
     }
 }
 
+// Attention of one query block over key tiles [job.kt0, job.kt0 + job.T):
+// the whole head (job.cut < 0: O is stored) or one piece of a split block.
 template <bool FUSEQ, bool STRIDED>
-__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int simd_of_wave[kWaves];
-
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *split_ticket, const SplitJob &job,
+                                         const int tid_in, const int group, const int gw) {
+  // lane constants are computed per job (an opaque copy of the thread id
+  // keeps them from being hoisted out of the job loop, where they would
+  // overlap the fused query transform's temporaries)
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
-
-  const int order = pingpong_order(simd_of_wave, wave, lane);
-  const int group = order & 1;
-  const int gw = order >> 1;                   // wave index inside the group
   const int rank = gw * 64 + lane;             // 0..255 inside the group
-
-  const int ntiles = (N + kBR - 1) / kBR;
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int bh = logical / ntiles;
-  const int qt = logical - bh * ntiles;
+  const int bh = job.bh, qt = job.qt, kt0 = job.kt0, T = job.T;
 
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 1, bh, a.H, N);
   const HeadView vk = head_view<STRIDED>(a.k, a.sk, 1, bh, a.H, N);
   const HeadView vv = head_view<STRIDED>(a.v, a.sv, 1, bh, a.H, N);
   const HeadView vo = head_view<STRIDED>(a.o, a.so, 2, bh, a.H, N);
 
-  const int T = (N + kBC - 1) / kBC;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
 
   // ---- lane constants (bytes).  Each group loads half of every tile:
@@ -264,30 +260,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
   // ---- ring traffic helpers
   auto k_dma = [&](const i32x4_t &words, uint32_t slot_bytes) __attribute__((always_inline)) {
-    const uint32_t m0 = k_m0 + slot_bytes;
+    // the LDS address is added up here, not by the compiler: precomputed
+    // sums for every slot would hold scalar registers through the loop
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_add_u32 m0, %0, %3\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(m0), "v"(k_dgoff), "s"(words)
-        : "memory");
+        : "s"(k_m0), "v"(k_dgoff), "s"(words), "s"(slot_bytes)
+        : "memory", "scc");
   };
   auto v_dma = [&](const i32x4_t &words, uint32_t slot_bytes) __attribute__((always_inline)) {
-    const uint32_t m0 = k_m0 + kVRingOffset + slot_bytes;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_add_u32 m0, %0, %3\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(m0), "v"(v_dgoff), "s"(words)
-        : "memory");
+        : "s"(k_m0), "v"(v_dgoff), "s"(words), "s"(kVRingOffset + slot_bytes)
+        : "memory", "scc");
   };
 
   // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
   for (int j = 0; j < 3 && j < T; ++j) {
-    k_dma(tile_words(vk, j, kBC), j * kKTileBytes);
-    v_dma(tile_words(vv, j, kBC), j * kVTileBytes);
+    k_dma(tile_words(vk, kt0 + j, kBC), j * kKTileBytes);
+    v_dma(tile_words(vv, kt0 + j, kBC), j * kVTileBytes);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -378,12 +374,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
     }
-    if (j * kBC + kBC > N) {
+    if ((kt0 + j) * kBC + kBC > N) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int key = (kt0 + j) * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
           if (key >= N) s[kb][r] = -INFINITY;
         }
     }
@@ -476,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
       if (step + kPre < 8) ring[step % kPre] = frag(step + kPre, kNext, kCur);
       matrix_step(step, f);
       if (step == 3) lsum = mfma16_f8(lones, pf, lsum);   // row sums of P(j)
-      if (step == kVLoadStep) v_dma(tile_words(vv, tn, kBC), kPlus3);
-      if (step == kKLoadStep) k_dma(tile_words(vk, tn, kBC), kPlus3);
+      if (step == kVLoadStep) v_dma(tile_words(vv, kt0 + tn, kBC), kPlus3);
+      if (step == kKLoadStep) k_dma(tile_words(vk, kt0 + tn, kBC), kPlus3);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -516,7 +512,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
   // ---- epilogue: O * s_v / l, one bf16 rounding; lane holds query l32 and
   // head dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end drop
-  const float l_run = lsum[0];   // all 64 keys of every tile, rounded P
+  float l_run = lsum[0];   // all 64 keys of every tile, rounded P
+  // a piece of a split block: the piece that finishes second merges
+  if (job.cut >= 0 && !split_merge(a, job, o, b_run, l_run, tid, split_ticket)) return;
   const float inv = o_scale / l_run;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
@@ -532,8 +530,37 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 }
 
 template <bool FUSEQ, bool STRIDED>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int simd_of_wave[kWaves];
+  __shared__ int split_ticket;
+
+  const int tid = threadIdx.x;
+  const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
+  const int group = order & 1;
+  const int gw = order >> 1;                   // wave index inside the group
+
+  // ---- this workgroup's share of the (query block, key tile) pairs; the
+  // range state waits in LDS (one copy per wave) while a job runs, so it
+  // takes no scalar registers there
+  __shared__ SplitRange range_lds[kWaves];
+  SplitRange *rs = &range_lds[tid >> 6];
+  {
+    const SplitRange r = split_range(a, kBR, kBC, xcd_logical_block(blockIdx.x, gridDim.x));
+    if ((tid & 63) == 0) *rs = r;
+  }
+  for (;;) {
+    SplitRange r = split_range_load(rs);
+    SplitJob job;
+    if (!split_next(r, job)) break;
+    if ((tid & 63) == 0) *rs = r;
+    attn_job<FUSEQ, STRIDED>(a, lds, &split_ticket, job, tid, group, gw);
+  }
+}
+
+template <bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
-  const int64_t grid = (int64_t)((a.N + kBR - 1) / kBR) * a.BH;
+  const int64_t grid = a.split_groups > 0 ? a.split_groups : (int64_t)((a.N + kBR - 1) / kBR) * a.BH;
   // Raise the dynamic-LDS limit once per device (idempotent, so a race
   // between threads only repeats the call).
   static std::atomic<uint64_t> attr_done{0};

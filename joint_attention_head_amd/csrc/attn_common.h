@@ -87,6 +87,166 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int total) {
   return xcd * q8 + min(xcd, r8) + (bid >> 3);
 }
 
+// ---- Key-range split.  Without a split, workgroup w computes query block
+// w whole (blocks in (b*h, query tile) order).  With split_groups = G
+// persistent workgroups and nb blocks (the host splits only when nb > G),
+// the first F = nb / G - 1 rounds go as whole blocks in launch order:
+// workgroup w takes blocks w, w + G, ..., so the workgroups running at one
+// time work on neighbouring blocks of the same heads and stream the same
+// key tiles in step, sharing them in L2.  The remaining nb - F G blocks
+// (between G and 2G - 1) form the tail: its (query block, key tile) pairs,
+// key tiles in order inside each block, are dealt out as G equal contiguous
+// shares, workgroup w taking share w.  Every share spans at least one
+// block's key tiles, so a tail block is cut at most once, between the
+// shares of workgroups w - 1 and w for cut index w.
+struct SplitRange {
+  int whole;          // whole blocks still to do before the tail
+  int blk, stride;    // next whole block, and the step between them
+  int64_t u, end;     // next pair of the tail share, end of the share
+  int key_tiles, q_tiles, logical;
+};
+struct SplitJob {
+  int bh, qt;         // head and query block
+  int kt0, T;         // key tiles [kt0, kt0 + T)
+  int cut;            // -1: the whole block; else the index of its cut
+  int piece;          // 0: keys before the cut, 1: after
+};
+
+__device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows, int keys, int logical) {
+  SplitRange r;
+  r.q_tiles = (a.N + rows - 1) / rows;
+  r.key_tiles = (a.N + keys - 1) / keys;
+  r.logical = logical;
+  r.blk = logical;
+  if (a.split_groups > 0) {
+    const int G = a.split_groups;
+    const int nb = a.BH * r.q_tiles;
+    r.whole = nb / G - 1;
+    r.stride = G;
+    const int64_t base = (int64_t)r.whole * G * r.key_tiles;
+    const int64_t U = (int64_t)(nb - r.whole * G) * r.key_tiles;
+    r.u = base + U * logical / G;
+    r.end = base + U * (logical + 1) / G;
+  } else {
+    r.whole = 1;
+    r.stride = 0;
+    r.u = r.end = 0;
+  }
+  return r;
+}
+
+// The range state back from LDS as wave-uniform (scalar) values.
+__device__ __forceinline__ SplitRange split_range_load(const SplitRange *p) {
+  auto u32 = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto u64 = [](int64_t v) {
+    const uint64_t x = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  SplitRange r;
+  r.whole = u32(p->whole);
+  r.blk = u32(p->blk);
+  r.stride = u32(p->stride);
+  r.u = u64(p->u);
+  r.end = u64(p->end);
+  r.key_tiles = u32(p->key_tiles);
+  r.q_tiles = u32(p->q_tiles);
+  r.logical = u32(p->logical);
+  return r;
+}
+
+// Next job of the workgroup (false when it is done).
+__device__ __forceinline__ bool split_next(SplitRange &r, SplitJob &j) {
+  int blk;
+  if (r.whole > 0) {
+    blk = r.blk;
+    r.blk += r.stride;
+    --r.whole;
+    j.kt0 = 0;
+    j.T = r.key_tiles;
+  } else {
+    if (r.u >= r.end) return false;
+    blk = (int)(r.u / r.key_tiles);
+    j.kt0 = (int)(r.u - (int64_t)blk * r.key_tiles);
+    j.T = (int)min((int64_t)(r.key_tiles - j.kt0), r.end - r.u);
+    r.u += j.T;
+  }
+  j.bh = blk / r.q_tiles;
+  j.qt = blk - j.bh * r.q_tiles;
+  j.piece = j.kt0 == 0 ? 0 : 1;
+  j.cut = j.T == r.key_tiles ? -1 : (j.piece == 0 ? r.logical + 1 : r.logical);
+  return true;
+}
+
+// End of one piece of a split block.  The piece stores its O accumulators
+// o (unnormalised, relative to 2^b: row shift b in base-2 units) and its
+// normaliser l, then counts itself in at the cut.  The first to arrive
+// returns false; the second reads the other piece and merges it into
+// (o, b, l), rescaling both to the larger shift, resets the count for the
+// next launch and returns true (it then stores O).  Nobody waits: the
+// merge happens in whichever order the pieces finish, and it is symmetric
+// in the two pieces, so the result does not depend on that order.
+// Coherence between the two workgroups (possibly on different XCDs, whose
+// L2 caches are not coherent with each other) comes from device-scope
+// accesses to the partials and the count alone: the partial stores and
+// loads carry the device-scope cache policy (sc1), the stores are retired
+// (vmcnt 0) before the workgroup barrier that precedes the count, and the
+// count is a device-scope atomic.  No cache-wide writeback or invalidate is
+// needed, so the other workgroups' cached K and V tiles stay put.  All
+// threads of the workgroup call this; it contains two workgroup barriers.
+constexpr int kCPolDevice = 16;   // buffer cache policy: sc1 (device scope)
+
+__device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob &job, f32x16_t (&o)[4], float &b,
+                                            float &l, int tid, int *ticket) {
+  constexpr uint32_t kPieceBytes = (uint32_t)(kSplitPieceFloats * 4);
+  const __amdgpu_buffer_rsrc_t mine =
+      make_rsrc(a.split_part + ((int64_t)job.cut * 2 + job.piece) * kSplitPieceFloats, kPieceBytes);
+  const __amdgpu_buffer_rsrc_t other =
+      make_rsrc(a.split_part + ((int64_t)job.cut * 2 + (job.piece ^ 1)) * kSplitPieceFloats, kPieceBytes);
+  const uint32_t t16 = (uint32_t)tid * 16u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int db = i >> 2, g = i & 3;
+    u32x4_t w;
+    w[0] = __float_as_uint(o[db][4 * g + 0]);
+    w[1] = __float_as_uint(o[db][4 * g + 1]);
+    w[2] = __float_as_uint(o[db][4 * g + 2]);
+    w[3] = __float_as_uint(o[db][4 * g + 3]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, mine, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
+  }
+  {
+    u32x2_t w;
+    w[0] = __float_as_uint(b);
+    w[1] = __float_as_uint(l);
+    __builtin_amdgcn_raw_buffer_store_b64(w, mine, 64u * 4u * kSplitThreads + (uint32_t)tid * 8u, 0, kCPolDevice);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) *ticket = __hip_atomic_fetch_add(a.split_cnt + job.cut, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*ticket == 0) return false;
+  if (tid == 0) __hip_atomic_store(a.split_cnt + job.cut, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(other, 64u * 4u * kSplitThreads + (uint32_t)tid * 8u, 0,
+                                                           kCPolDevice);
+  u32x4_t x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    x[i] = __builtin_amdgcn_raw_buffer_load_b128(other, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
+  const float b2 = __uint_as_float(blw[0]), l2 = __uint_as_float(blw[1]);
+  const float m = fmaxf(b, b2);
+  const float sa = __builtin_amdgcn_exp2f(b - m), sb = __builtin_amdgcn_exp2f(b2 - m);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int db = i >> 2, g = i & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[db][4 * g + e] = o[db][4 * g + e] * sa + __uint_as_float(x[i][e]) * sb;
+  }
+  l = l * sa + l2 * sb;
+  b = m;
+  return true;
+}
+
 // One (b,h) head of a [B,H,N,D] view: base pointer, bytes per token row,
 // and the buffer extent (ends with row N-1, so rows past N read as zero
 // and stores there are dropped).

@@ -64,7 +64,23 @@ struct ForwardArgs {
   float eps;
   int32_t rope_first[4];
   float rope_log2_step[3];
+  // Key-range split (split_groups > 0): a persistent grid of split_groups
+  // workgroups, each taking an equal contiguous share of the
+  // (query block, key tile) pairs.  A query block cut between two
+  // workgroups leaves one partial result per piece in split_part; the
+  // second piece to finish merges them (split_cnt holds the arrival count
+  // of each cut and is left at zero).
+  float *split_part;
+  int32_t *split_cnt;
+  int32_t split_groups;
 };
+
+// Partial result of one piece of a split query block: per thread of the
+// 512-thread workgroup, 64 fp32 O accumulators (16 float4, stored
+// [float4 index][thread]) then the row shift b and normaliser l (float2
+// per thread).  Two pieces per cut.
+constexpr int kSplitThreads = 512;
+constexpr int64_t kSplitPieceFloats = (int64_t)kSplitThreads * 64 + (int64_t)kSplitThreads * 2;
 
 hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
                                 hipStream_t s);
@@ -77,7 +93,9 @@ hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
 hipError_t launch_forward_bf16(const ForwardArgs &a, bool fused, bool strided, hipStream_t s);
 hipError_t launch_forward_fp8(const ForwardArgs &a, bool fused, bool strided, hipStream_t s);
 
-// Workgroups the forward kernel launches for B*H heads of N tokens.
+// Query blocks (one workgroup each without a split) for B*H heads of N
+// tokens, and key tiles per head.
 int64_t forward_grid_blocks(int64_t BH, int64_t N);
+int64_t forward_key_tiles(int64_t N);
 
 }  // namespace fluxattn

@@ -95,6 +95,21 @@ def fused8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, o=O, wq=WQ, pos=POS, b=B, h=
                                           0.0, None)
 
 
+def test_forward_groups_setting(lib):
+    """Host-only setting: round-trips, rejects counts above 16384 and keeps
+    the previous value then."""
+    assert lib.fluxattn_get_forward_groups() == 0          # default
+    try:
+        for g in (-1, 3, 256, 16384, 0):
+            assert lib.fluxattn_set_forward_groups(g) == OK
+            assert lib.fluxattn_get_forward_groups() == g
+        assert lib.fluxattn_set_forward_groups(5) == OK
+        assert lib.fluxattn_set_forward_groups(16385) == SHAPE
+        assert lib.fluxattn_get_forward_groups() == 5
+    finally:
+        lib.fluxattn_set_forward_groups(0)
+
+
 def test_null_pointers(lib):
     for kw in ("q", "k", "qo", "ko", "wq", "wk", "pos"):
         assert prologue(lib, **{kw: None}) == NULLP, kw

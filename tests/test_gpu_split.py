@@ -1,0 +1,190 @@
+"""Key-range split of the attention launches, through the C ABI.
+
+With G persistent workgroups each taking an equal share of the (query
+block, key tile) pairs, a query block can be computed in two key ranges
+whose partial results the second piece to finish merges.  The split is
+forced here at sizes the fp64 oracle handles by setting G below the number
+of 256-query blocks; every case spans several 64-key tiles, with a ragged
+last key tile and a ragged last query block.  Checked: parity with the
+oracle (same tolerances as the uncut launch), closeness to the uncut launch
+(a piece that starts inside a block takes its first row shift from its own
+first tile, so its P values are rounded relative to another shift: the two
+launches differ by that rounding and fp32 summation order, far inside the
+oracle tolerance), bitwise determinism (the merge is symmetric in the two
+pieces, so arrival order does not matter), and that a launch leaves the
+arrival counts at zero (a later launch on other inputs is still right).
+"""
+import contextlib
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_head_amd as fa
+import oracle
+from workloads import custom_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BF16_TOL = (2e-2, 2e-3)
+FP8_TOL = (4e-2, 4e-3)
+
+# (B, H, text tokens, image grid): N = 1000 (8 query blocks, 16 key tiles,
+# the last one 40 keys) and N = 667 (18 blocks, 11 tiles, the last 27 keys)
+SHAPES = {"n1000": (1, 2, 40, (24, 40)), "n667": (2, 3, 7, (20, 33))}
+GROUPS = (2, 3, 5, 7)
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+@contextlib.contextmanager
+def forward_groups(g):
+    old = fa.fluxattn_get_forward_groups()
+    fa.fluxattn_set_forward_groups(g)
+    try:
+        yield
+    finally:
+        fa.fluxattn_set_forward_groups(old)
+
+
+def inputs(shape, dtype="bf16", seed=0):
+    B, H, n_txt, grid = SHAPES[shape]
+    return make_inputs(custom_workload(B, H, n_txt, grid, None, dtype, seed))
+
+
+def dev(t):
+    return t.to(DEV).contiguous()
+
+
+def f64(t, scale=None):
+    return oracle.torch_to_f64(t.cpu() if t.is_cuda else t, None if scale is None else scale.cpu())
+
+
+def check_close(got, ref, tol, what):
+    err = np.abs(got - ref)
+    _flush(f"{what}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+    assert np.isfinite(got).all(), what
+    assert err.max() <= tol[0], (what, err.max())
+    assert err.mean() <= tol[1], (what, err.mean())
+
+
+# split vs uncut launch: P rounding (bf16: 2^-9 relative, E4M3: 2^-4) of
+# the same probabilities against another row shift
+UNCUT_TOL = {"bf16": (4e-3, 2e-4), "fp8": (2e-2, 2e-3)}
+
+
+def close_to_uncut(a, b, dtype, what):
+    d = np.abs(f64(a) - f64(b))
+    _flush(f"{what}: split vs uncut max diff {d.max():.3e} mean {d.mean():.3e}")
+    assert d.max() <= UNCUT_TOL[dtype][0], what
+    assert d.mean() <= UNCUT_TOL[dtype][1], what
+
+
+def n_blocks(inp):
+    B, H, N = inp.q.shape[:3]
+    return B * H * ((N + 255) // 256)
+
+
+def forward_bf16(inp):
+    return fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), dev(inp.v))
+
+
+def joint_bf16(inp):
+    return fa.fluxattn_joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k),
+                                            dev(inp.pos))
+
+
+def forward_fp8(inp):
+    return fa.fluxattn_forward_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale),
+                                   dev(inp.v_scale))
+
+
+def joint_fp8(inp):
+    return fa.fluxattn_joint_attention_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale),
+                                           dev(inp.k_scale), dev(inp.v_scale), dev(inp.w_q), dev(inp.w_k),
+                                           dev(inp.pos))
+
+
+def attention_ref(inp):
+    if inp.q.dtype == torch.float8_e4m3fn:
+        return oracle.attention(f64(inp.q, inp.q_scale), f64(inp.k, inp.k_scale), f64(inp.v, inp.v_scale))
+    return oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v))
+
+
+def joint_ref(inp):
+    sc = lambda t, s: f64(t, s) if t.dtype == torch.float8_e4m3fn else f64(t)
+    return oracle.joint_attention(sc(inp.q, inp.q_scale), sc(inp.k, inp.k_scale), sc(inp.v, inp.v_scale),
+                                  inp.w_q.double().numpy(), inp.w_k.double().numpy(), inp.pos.numpy())
+
+
+PATHS = {
+    "forward_bf16": (forward_bf16, attention_ref, "bf16", BF16_TOL),
+    "joint_fused_bf16": (joint_bf16, joint_ref, "bf16", BF16_TOL),
+    "forward_fp8": (forward_fp8, attention_ref, "fp8", FP8_TOL),
+    "joint_fused_fp8": (joint_fp8, joint_ref, "fp8", FP8_TOL),
+}
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("path", list(PATHS))
+def test_split_matches_oracle_and_uncut_launch(path, shape):
+    run, ref_fn, dtype, tol = PATHS[path]
+    inp = inputs(shape, dtype)
+    assert n_blocks(inp) > max(GROUPS)
+    ref = ref_fn(inp)
+    with forward_groups(-1):
+        whole = run(inp)
+    for g in GROUPS:
+        _flush(f"split {path} {shape} groups={g}")
+        with forward_groups(g):
+            o = run(inp)
+        torch.cuda.synchronize()
+        check_close(f64(o), ref, tol, f"split {path} {shape} G={g}")
+        close_to_uncut(o, whole, dtype, f"split {path} {shape} G={g}")
+
+
+def test_split_is_deterministic_and_leaves_counts_at_zero():
+    a, b = inputs("n1000", seed=0), inputs("n1000", seed=5)
+    with forward_groups(3):
+        o1 = forward_bf16(a)
+        ob = forward_bf16(b)     # other inputs: stale counts would merge a's partials
+        o2 = forward_bf16(a)
+    torch.cuda.synchronize()
+    check_close(f64(ob), attention_ref(b), BF16_TOL, "split second launch, other inputs")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_split_strided_layout():
+    """The ex entry point on [B, N, H, D] storage (token-major), cut."""
+    inp = inputs("n667")
+    B, H, N, D = inp.q.shape
+    tm = lambda t: t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    q, k, v = tm(inp.q), tm(inp.k), tm(inp.v)
+    o = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    with forward_groups(5):
+        fa.fluxattn_forward_ex_bf16(q, k, v, o=o)
+    torch.cuda.synchronize()
+    check_close(f64(o), attention_ref(inp), BF16_TOL, "split strided n667 G=5")
+
+
+def test_split_default_setting_flux_dev_1024():
+    """FLUX-dev 1024x1024 (B=1, H=24, N=4608: 432 query blocks): the default
+    setting cuts blocks on a device with fewer compute units than blocks;
+    the result is close to the uncut launch and matches the oracle on
+    sampled rows of two heads."""
+    w = custom_workload(1, 24, 512, (64, 64))
+    inp = make_inputs(w)
+    with forward_groups(0):
+        o = forward_bf16(inp)
+    with forward_groups(-1):
+        whole = forward_bf16(inp)
+    torch.cuda.synchronize()
+    close_to_uncut(o, whole, "bf16", "default setting N=4608")
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(4560, 4608), np.arange(0, 4608, 97)]))
+    for h in (0, 23):
+        sl = (slice(0, 1), slice(h, h + 1))
+        ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
+        check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"default setting N=4608 head {h}")
