@@ -202,11 +202,13 @@ fluxattn_status fluxattn_forward_fp8(
  *   softmax_scale  as in fluxattn_forward_bf16.
  * Q' is computed in fp32, multiplied by c = softmax scale * log2 e and
  * rounded to bf16 once (the prologue rounds Q' itself once), so the QK^T
- * product yields base-2 logits directly.  The rotation frequencies are 2^(j * -2 log2(theta) / axes_a)
- * evaluated on the device (within 1e-6 relative of the host table the
- * prologue uses) and the angles go through the hardware sine / cosine
- * after reduction to one revolution (absolute error about
- * 1e-6 + 4e-8 |angle| rad).  Numerics otherwise as fluxattn_forward_bf16.
+ * product yields base-2 logits directly.  The rotation rates are the
+ * prologue's frequencies theta^(-2j/axes_a) computed on the host and
+ * expressed in revolutions (divided by 2 pi, rounded to fp32); each angle
+ * pos * rate is reduced to one revolution and goes through the hardware
+ * sine / cosine (absolute error about 1e-6 + 1.2e-7 |angle| rad, the fp32
+ * rounding of the rate and of the product).  Numerics
+ * otherwise as fluxattn_forward_bf16.
  */
 fluxattn_status fluxattn_forward_fused_bf16(
     const void *q, const void *k, const void *v, void *o,

@@ -443,13 +443,16 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
     a.pos = pos_ids;
     a.eps = eps;
     a.streams = to_streams(streams);
+    // the key prologue's frequencies (make_rope_table), in revolutions
     const int32_t dims[3] = {at, ah, aw};
-    a.rope_first[0] = 0;
-    for (int i = 0; i < 3; ++i) {
-      a.rope_first[i + 1] = a.rope_first[i] + dims[i] / 2;
-      a.rope_log2_step[i] =
-          dims[i] > 0 ? static_cast<float>(-2.0 * log2(static_cast<double>(theta)) / dims[i]) : 0.f;
-    }
+    int pair = 0;
+    for (int ax = 0; ax < 3; ++ax)
+      for (int j = 0; j < dims[ax] / 2; ++j, ++pair) {
+        for (int b = 0; b < 3; ++b)
+          a.rope_rate[b][pair] =
+              b == ax ? static_cast<float>(pow(static_cast<double>(theta), -2.0 * j / dims[ax]) / 6.283185307179586)
+                      : 0.f;
+      }
   }
   const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
                          is_contiguous(o, H, N, D));

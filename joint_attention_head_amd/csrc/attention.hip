@@ -102,8 +102,8 @@ __device__ __forceinline__ bf16x8_t lds_read_tr2(const char *p) {
 // 16 kk + 8 hi + i; the other 64 are in lane ^ 32) -> times c = softmax
 // scale * log2 e -> bf16, so that the QK^T MFMA yields base-2 logits.  The
 // one bf16 rounding of Q' is the same as the prologue's, applied to c Q'.
-__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const HeadView &vq, int q_row,
-                                             int hi) {
+__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const RopeLds *rope,
+                                             const HeadView &vq, int q_row, int hi) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -122,11 +122,13 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
     ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
   }
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  // rstd and the logit scale c folded into the weights: Q' c = (x w rstd c)
+  // rotated
+  const float rs = a.scale_log2 / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
   // position ids of this query (rows past N belong to no token: any valid
   // row serves, their outputs are never stored)
   const int tok = min(q_row, a.N - 1);
-  const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
+  const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
   const float *w_q = stream_weights(a, tok);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -136,23 +138,21 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArg
     const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi);
     const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi + 4);
     const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float sn[4], cs[4];
+    rotations4(rope, pf, 8 * kk + 4 * hi, sn, cs);   // pairs 8 kk + 4 hi + m
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      float sn, cs;
-      pair_rotation(a, pos, 8 * kk + 4 * hi + m, sn, cs);
-      const float u = x[2 * m] * w[2 * m] * rstd;
-      const float v = x[2 * m + 1] * w[2 * m + 1] * rstd;
-      qf[kk][2 * m] = (__bf16)((u * cs - v * sn) * a.scale_log2);
-      qf[kk][2 * m + 1] = (__bf16)((u * sn + v * cs) * a.scale_log2);
+      const float u = x[2 * m] * (w[2 * m] * rs);
+      const float v = x[2 * m + 1] * (w[2 * m + 1] * rs);
+      qf[kk][2 * m] = (__bf16)(u * cs[m] - v * sn[m]);
+      qf[kk][2 * m + 1] = (__bf16)(u * sn[m] + v * cs[m]);
     }
   }
 }
 
-// Attention of one query block over key tiles [job.kt0, job.kt0 + job.T):
-// the whole head (job.cut < 0: O is stored) or one piece of a split block.
 template <bool FUSEQ, bool STRIDED>
-__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *split_ticket, const SplitJob &job,
-                                         const int tid_in, const int group, const int gw) {
+__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const RopeLds *rope, int *split_ticket,
+                                         const SplitJob &job, const int tid_in, const int group, const int gw) {
   // lane constants are computed per job (an opaque copy of the thread id
   // keeps them from being hoisted out of the job loop, where they would
   // overlap the fused query transform's temporaries)
@@ -170,7 +170,7 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *s
   const int q_row = qt * kBR + wave * 32 + l32;
   bf16x8_t qf[8];
   if constexpr (FUSEQ) {
-    load_q_fused(qf, a, vq, q_row, hi);
+    load_q_fused(qf, a, rope, vq, q_row, hi);
   } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
@@ -504,8 +504,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int simd_of_wave[kWaves];
   __shared__ int split_ticket;
+  __shared__ RopeLds rope;
 
   const int tid = threadIdx.x;
+  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid);   // before the barrier in pingpong_order
   // ---- ping-pong groups: the two waves of a SIMD land in different groups
   const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
   const int group = order & 1;
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
     SplitJob job;
     if (!split_next(r, job)) break;
     if ((tid & 63) == 0) *rs = r;
-    attn_job<FUSEQ, STRIDED>(a, lds, &split_ticket, job, tid, group, gw);
+    attn_job<FUSEQ, STRIDED>(a, lds, &rope, &split_ticket, job, tid, group, gw);
   }
 }
 

@@ -123,7 +123,8 @@ __device__ __forceinline__ f32x16_t mfma_f8_bscaled(i32x8_t a, i32x8_t b, f32x16
 // logits c*S directly, and the largest code of the query lies in (224, 448].
 // Returns the E8M0 scale 127 + e in `sb`.  The lane holds dims
 // 64 kk + 32 hi + (0..31); the other 64 are in lane ^ 32.
-__device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const ForwardArgs &a, const HeadView &vq,
+__device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const ForwardArgs &a, const RopeLds *rope,
+                                             const HeadView &vq,
                                              int q_row, int hi, float in_scale, float g) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
   u32x4_t raw[4];   // raw[2 kk + t]: dims 64 kk + 32 hi + 16 t + (0..15)
@@ -132,6 +133,8 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
     raw[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                              rq, (uint32_t)q_row * vq.row + (uint32_t)(64 * (c >> 1) + 32 * hi + 16 * (c & 1)),
                                              0, 0));
+  // E4M3 codes as float; the dequantisation scale s_q is folded into the
+  // normalisation: x_deq w rstd = x w (s_q rstd), with rstd from s_q^2 sum x^2
   float x[64];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -139,10 +142,10 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
     for (int w = 0; w < 4; ++w) {
       const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[c][w], false);
       const f32x2_t up = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[c][w], true);
-      x[16 * c + 4 * w + 0] = lo[0] * in_scale;
-      x[16 * c + 4 * w + 1] = lo[1] * in_scale;
-      x[16 * c + 4 * w + 2] = up[0] * in_scale;
-      x[16 * c + 4 * w + 3] = up[1] * in_scale;
+      x[16 * c + 4 * w + 0] = lo[0];
+      x[16 * c + 4 * w + 1] = lo[1];
+      x[16 * c + 4 * w + 2] = up[0];
+      x[16 * c + 4 * w + 3] = up[1];
     }
   float ss = 0.f;
 #pragma unroll
@@ -151,30 +154,35 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
     ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
   }
-  const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  const float rs = in_scale / sqrtf(ss * (in_scale * in_scale) * (1.0f / kHeadDim) + a.eps);
   // rows past N belong to no token: any valid row serves, their outputs are
   // never stored
   const int tok = min(q_row, a.N - 1);
-  const int32_t pos[3] = {a.pos[3 * tok + 0], a.pos[3 * tok + 1], a.pos[3 * tok + 2]};
+  const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
   const float *w_q = stream_weights(a, tok);
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d0 = 64 * (c >> 1) + 32 * hi + 16 * (c & 1);   // first dim of this chunk
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 w = *reinterpret_cast<const float4 *>(w_q + d0 + 4 * q4);
-      const float wv[4] = {w.x, w.y, w.z, w.w};
+    for (int g = 0; g < 2; ++g) {
+      // pairs d0 / 2 + 4 g + (0..3)
+      float sn[4], cs[4];
+      rotations4(rope, pf, 32 * (c >> 1) + 16 * hi + 8 * (c & 1) + 4 * g, sn, cs);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float sn, cs;
-        pair_rotation(a, pos, (d0 + 4 * q4 + 2 * m) >> 1, sn, cs);
-        const int i = 16 * c + 4 * q4 + 2 * m;
-        const float u = x[i] * wv[2 * m] * rstd;
-        const float v = x[i + 1] * wv[2 * m + 1] * rstd;
-        x[i] = u * cs - v * sn;
-        x[i + 1] = u * sn + v * cs;
-        amax = fmaxf(amax, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q4 = 2 * g + qq;
+        const float4 w = *reinterpret_cast<const float4 *>(w_q + d0 + 4 * q4);
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int i = 16 * c + 4 * q4 + 2 * m, r = 2 * qq + m;
+          const float u = x[i] * (wv[2 * m] * rs);
+          const float v = x[i + 1] * (wv[2 * m + 1] * rs);
+          x[i] = u * cs[r] - v * sn[r];
+          x[i + 1] = u * sn[r] + v * cs[r];
+          amax = fmaxf(amax, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+        }
       }
     }
   }
@@ -206,8 +214,8 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
 // Attention of one query block over key tiles [job.kt0, job.kt0 + job.T):
 // the whole head (job.cut < 0: O is stored) or one piece of a split block.
 template <bool FUSEQ, bool STRIDED>
-__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *split_ticket, const SplitJob &job,
-                                         const int tid_in, const int group, const int gw) {
+__device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const RopeLds *rope, int *split_ticket,
+                                         const SplitJob &job, const int tid_in, const int group, const int gw) {
   // lane constants are computed per job (an opaque copy of the thread id
   // keeps them from being hoisted out of the job loop, where they would
   // overlap the fused query transform's temporaries)
@@ -294,7 +302,7 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, int *s
   float qs = 1.f;
   int qsb = 127;   // fused: E8M0 B scale of the QK^T MFMAs, c folded in
   if constexpr (FUSEQ) {
-    load_q_fused(qf, qsb, a, vq, q_row, hi, a.q_scale[bh], a.scale_log2 * a.k_scale[bh]);
+    load_q_fused(qf, qsb, a, rope, vq, q_row, hi, a.q_scale[bh], a.scale_log2 * a.k_scale[bh]);
   } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
@@ -534,8 +542,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int simd_of_wave[kWaves];
   __shared__ int split_ticket;
+  __shared__ RopeLds rope;
 
   const int tid = threadIdx.x;
+  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid);   // before the barrier in pingpong_order
   const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
   const int group = order & 1;
   const int gw = order >> 1;                   // wave index inside the group
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
     SplitJob job;
     if (!split_next(r, job)) break;
     if ((tid & 63) == 0) *rs = r;
-    attn_job<FUSEQ, STRIDED>(a, lds, &split_ticket, job, tid, group, gw);
+    attn_job<FUSEQ, STRIDED>(a, lds, &rope, &split_ticket, job, tid, group, gw);
   }
 }
 

@@ -287,20 +287,38 @@ __device__ __forceinline__ const float *stream_weights(const ForwardArgs &a, int
   return a.w_q + sid * kHeadDim;
 }
 
-// Rotation angle of head-dim pair `pr` of a token at positions pos[3], as
-// (sin, cos): the frequency is 2^(j * rope_log2_step[axis]) for the pair's
-// index j inside its axis block; the angle is reduced to [0, 1) revolutions
-// and fed to the hardware sin / cos (absolute error about 1e-6 + 4e-8 |angle|
-// rad, the size of the fp32 rounding of the angle itself at FLUX's positions).
-__device__ __forceinline__ void pair_rotation(const ForwardArgs &a, const int32_t (&pos)[3], int pr, float &sn,
-                                              float &cs) {
-  const int ax = pr < a.rope_first[1] ? 0 : (pr < a.rope_first[2] ? 1 : 2);
-  const int jj = pr - (ax == 0 ? 0 : (ax == 1 ? a.rope_first[1] : a.rope_first[2]));
-  const float step = ax == 0 ? a.rope_log2_step[0] : (ax == 1 ? a.rope_log2_step[1] : a.rope_log2_step[2]);
-  const int32_t p = ax == 0 ? pos[0] : (ax == 1 ? pos[1] : pos[2]);
-  const float rev = __builtin_amdgcn_fractf((float)p * exp2f((float)jj * step) * 0.15915494309189535f);
-  sn = __builtin_amdgcn_sinf(rev);
-  cs = __builtin_amdgcn_cosf(rev);
+// Rotation rates of the fused query prologue in LDS: rate[a][p] as in the
+// arguments (one nonzero axis per pair).  Filled by threads 0..63 before
+// the workgroup's first barrier.
+struct alignas(16) RopeLds {
+  float rate[3][kPairs];
+};
+
+__device__ __forceinline__ void rope_lds_fill(RopeLds *t, const ForwardArgs &a, int tid) {
+  if (tid < kPairs) {
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) t->rate[ax][tid] = a.rope_rate[ax][tid];
+  }
+}
+
+// (sin, cos) of the rotations of pairs p0 .. p0+3 (p0 a multiple of 4) of a
+// token at positions pf: angle = sum over axes of pf[a] * rate[a][p] in
+// revolutions (two of the three products are exactly 0, so this is the one
+// product of the pair's own axis), reduced to [0, 1) for the hardware sine
+// / cosine (absolute error about 1e-6 plus the fp32 rounding of the
+// product, 6e-8 of it).
+__device__ __forceinline__ void rotations4(const RopeLds *t, const float (&pf)[3], int p0, float (&sn)[4],
+                                           float (&cs)[4]) {
+  const float4 r0 = *reinterpret_cast<const float4 *>(&t->rate[0][p0]);
+  const float4 r1 = *reinterpret_cast<const float4 *>(&t->rate[1][p0]);
+  const float4 r2 = *reinterpret_cast<const float4 *>(&t->rate[2][p0]);
+  const float a0[4] = {r0.x, r0.y, r0.z, r0.w}, a1[4] = {r1.x, r1.y, r1.z, r1.w}, a2[4] = {r2.x, r2.y, r2.z, r2.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float rev = __builtin_amdgcn_fractf(fmaf(pf[2], a2[m], fmaf(pf[1], a1[m], pf[0] * a0[m])));
+    sn[m] = __builtin_amdgcn_sinf(rev);
+    cs[m] = __builtin_amdgcn_cosf(rev);
+  }
 }
 
 }  // namespace attn

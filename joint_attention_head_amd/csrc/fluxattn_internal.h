@@ -55,15 +55,15 @@ struct ForwardArgs {
   float scale_log2;   // softmax_scale * log2(e)
   Strides sq, sk, sv, so;   // used by the strided kernels only
   Streams streams;          // fused query prologue only
-  // fused query prologue only: raw q is normalised and rotated on load.
-  // Pair p of axis a (pairs rope_first[a] .. rope_first[a+1]-1) turns by
-  // pos[a] * 2^((p - rope_first[a]) * rope_log2_step[a]), with
-  // rope_log2_step[a] = -2 log2(theta) / axes[a].
+  // fused query prologue only: raw q is normalised and rotated on load
   const float *w_q;
   const int32_t *pos;
   float eps;
-  int32_t rope_first[4];
-  float rope_log2_step[3];
+  // pair p turns by pos[a] * rope_rate[a][p] revolutions summed over the
+  // three axes a: rope_rate[a][p] = theta^(-2 j / axes[a]) / (2 pi) for the
+  // axis a that pair p belongs to (index j inside it), 0 for the other two
+  // (the key prologue's frequencies, in revolutions)
+  float rope_rate[3][kPairs];
   // Key-range split (split_groups > 0): a persistent grid of split_groups
   // workgroups, each taking an equal contiguous share of the
   // (query block, key tile) pairs.  A query block cut between two
