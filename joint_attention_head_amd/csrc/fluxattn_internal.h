@@ -42,7 +42,7 @@ struct PrologueArgs {
   Strides sq, sk, sqo, sko;
   Streams streams;
   int32_t num_streams;
-  int32_t bh_chunk;                   // fp8 kernel: (b,h) rows per block along grid.y
+  int32_t bh_chunk;                   // (b,h) rows per block along grid.y
 };
 
 struct ForwardArgs {

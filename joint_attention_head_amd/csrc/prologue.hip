@@ -10,8 +10,11 @@
 // group g (16 lanes) holds token g, and lane c of the group owns head dims
 // [8c, 8c+8) = rotation pairs 4c..4c+3.  The four rotation angles of a lane
 // depend only on its token, so their sin/cos are evaluated once and reused
-// for all B*H rows of Q and of K.  For a fixed (b,h) the block reads and
-// writes one contiguous 4 KiB (bf16) or 2 KiB (fp8) span.
+// for the (b,h) rows of Q and of K that the block walks: all of them, or a
+// chunk of them per grid.y index where the token blocks alone would leave
+// the chip short of work (bf16: fewer than about 1024 blocks).  For a fixed
+// (b,h) the block reads and writes one contiguous 4 KiB (bf16) or 2 KiB
+// (fp8) span.
 #include "fluxattn_internal.h"
 
 #include <algorithm>
@@ -124,6 +127,8 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
   float cs[4], sn[4];
   lane_angles(a, t, tok, c, cs, sn);
 
+  const int64_t bh_begin = (int64_t)blockIdx.y * a.bh_chunk;
+  const int64_t bh_end = min((int64_t)a.BH, bh_begin + a.bh_chunk);
   const int sid = stream_of(a.streams, tok);
   for (int which = a.q ? 0 : 1; which < 2; ++which) {   // no q: keys only
     const uint16_t *src = static_cast<const uint16_t *>(which ? a.k : a.q);
@@ -136,8 +141,14 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
     for (int i = 0; i < 8; ++i) w[i] = wp[8 * c + i];
 
     const int64_t tin = (int64_t)tok * si.n + 8 * c, tout = (int64_t)tok * so.n + 8 * c;
-    HeadWalk walk{0, 0, 0};
-    for (int64_t bh0 = 0; bh0 < a.BH; bh0 += kUnroll) {
+    HeadWalk walk;
+    {
+      const int64_t b = bh_begin / a.H, h = bh_begin - b * a.H;
+      walk.in = b * si.b + h * si.h;
+      walk.out = b * so.b + h * so.h;
+      walk.h = (int32_t)h;
+    }
+    for (int64_t bh0 = bh_begin; bh0 < bh_end; bh0 += kUnroll) {
       int64_t oin[kUnroll], oout[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -148,10 +159,10 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(PrologueArgs a,
       uint4 x[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (bh0 + u < a.BH) x[u] = *reinterpret_cast<const uint4 *>(src + oin[u]);
+        if (bh0 + u < bh_end) x[u] = *reinterpret_cast<const uint4 *>(src + oin[u]);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (bh0 + u >= a.BH) break;
+        if (bh0 + u >= bh_end) break;
         float f[8] = {bf16_lo(x[u].x), bf16_hi(x[u].x), bf16_lo(x[u].y), bf16_hi(x[u].y),
                       bf16_lo(x[u].z), bf16_hi(x[u].z), bf16_lo(x[u].w), bf16_hi(x[u].w)};
         norm_rope8(f, w, cs, sn, a.eps);
@@ -184,12 +195,11 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(const float *f) {
 
 // fp8 rows are 128 B: 8 lanes per token, 16 codes (8 rotation pairs) per
 // lane, so every lane moves 16 bytes per load and store; 32 tokens per block.
-// The (b,h) rows are split over grid.y in chunks of a.bh_chunk (16, more
-// only where grid.y would pass its limit), which gives the half-size fp8
-// stream enough blocks in flight.
+// The (b,h) rows are split over grid.y in chunks of a.bh_chunk (sized on
+// the host for about eight blocks per compute unit), which gives the
+// half-size fp8 stream enough blocks in flight.
 constexpr int kLanes8 = 8;
 constexpr int kTokensPerBlock8 = kThreads / kLanes8;
-constexpr int kChunk8 = 16;
 constexpr int64_t kMaxGridY = 65535;
 
 __device__ __forceinline__ float row8_sum(float x) {
@@ -315,16 +325,30 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
 
 }  // namespace
 
+// (b,h) rows per block along grid.y for bx token blocks: the fewest chunks
+// that give about `blocks` blocks in all, each a multiple of the 4-row
+// unroll, and grid.y within its limit
+int32_t bh_chunk_for(int64_t BH, int64_t bx, int64_t blocks) {
+  const int64_t want = std::max<int64_t>(1, (blocks + bx - 1) / bx);
+  int64_t chunk = (BH + want - 1) / want;
+  chunk = (chunk + kUnroll - 1) / kUnroll * kUnroll;
+  return (int32_t)std::max<int64_t>(chunk, (BH + kMaxGridY - 1) / kMaxGridY);
+}
+
 hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
-  const dim3 grid((a.N + kTokensPerBlock - 1) / kTokensPerBlock);
-  hipLaunchKernelGGL(prologue_bf16_kernel, grid, dim3(kThreads), 0, s, a, t);
+  PrologueArgs b = a;
+  const int64_t bx = (a.N + kTokensPerBlock - 1) / kTokensPerBlock;
+  b.bh_chunk = bh_chunk_for(a.BH, bx, 1024);   // about four blocks per compute unit
+  const dim3 grid((unsigned)bx, (unsigned)((a.BH + b.bh_chunk - 1) / b.bh_chunk));
+  hipLaunchKernelGGL(prologue_bf16_kernel, grid, dim3(kThreads), 0, s, b, t);
   return hipGetLastError();
 }
 
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
   PrologueArgs b = a;
-  b.bh_chunk = (int32_t)std::max<int64_t>(kChunk8, (a.BH + kMaxGridY - 1) / kMaxGridY);
-  const dim3 grid((a.N + kTokensPerBlock8 - 1) / kTokensPerBlock8, (unsigned)((a.BH + b.bh_chunk - 1) / b.bh_chunk));
+  const int64_t bx = (a.N + kTokensPerBlock8 - 1) / kTokensPerBlock8;
+  b.bh_chunk = bh_chunk_for(a.BH, bx, 2048);   // the half-size fp8 stream: eight per compute unit
+  const dim3 grid((unsigned)bx, (unsigned)((a.BH + b.bh_chunk - 1) / b.bh_chunk));
   hipLaunchKernelGGL(prologue_fp8_kernel, grid, dim3(kThreads), 0, s, b, t);
   return hipGetLastError();
 }
