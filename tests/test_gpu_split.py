@@ -188,3 +188,29 @@ def test_split_default_setting_flux_dev_1024():
         sl = (slice(0, 1), slice(h, h + 1))
         ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
         check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"default setting N=4608 head {h}")
+
+
+def test_split_on_two_streams_at_once():
+    """Each stream has its own split workspace: cut launches on two streams
+    that run at the same time give bitwise the results of running them one
+    after the other."""
+    a, b = inputs("n1000", seed=0), inputs("n1000", seed=7)
+    qa, ka, va = dev(a.q), dev(a.k), dev(a.v)
+    qb, kb, vb = dev(b.q), dev(b.k), dev(b.v)
+    with forward_groups(3):
+        ref_a = fa.fluxattn_forward_bf16(qa, ka, va)
+        ref_b = fa.fluxattn_forward_bf16(qb, kb, vb)
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = []
+        for _ in range(4):
+            with torch.cuda.stream(s1):
+                oa = fa.fluxattn_forward_bf16(qa, ka, va)
+            with torch.cuda.stream(s2):
+                ob = fa.fluxattn_forward_bf16(qb, kb, vb)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
+        assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
+    check_close(f64(ref_b), attention_ref(b), BF16_TOL, "split, second stream's inputs")
