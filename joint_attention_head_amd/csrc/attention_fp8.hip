@@ -498,8 +498,18 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
 
   __syncthreads();
   if (group == 1) __syncthreads();
+  // QK^T(0): all four fragments requested before the first MFMA
+  {
+    i32x8_t r0[4];
 #pragma unroll
-  for (int step = 4; step < 8; ++step) matrix_step(step, frag(step, 0, 0));
+    for (int i = 0; i < 4; ++i) r0[i] = frag(4 + i, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 4; step < 8; ++step) {
+      matrix_step(step, r0[step - 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   __syncthreads();
   i32x8_t ring[kPre];
   prefetch(1 * kKTileBytes, 0, ring);
