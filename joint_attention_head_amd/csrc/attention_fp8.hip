@@ -37,6 +37,9 @@
 //    raw E4M3 queries, applies RMSNorm + RoPE in fp32 and re-encodes each
 //    query with its own power-of-two scale, which the QK^T MFMA applies as
 //    its B block scale together with the softmax scale.
+//  * Work per workgroup: a list of jobs, one whole query block or, when
+//    the host balances the last round, pieces of blocks split by key
+//    range, as in the bf16 kernel (attn_common.h).
 #include "attn_common.h"
 
 #include <atomic>
