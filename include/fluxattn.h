@@ -343,23 +343,30 @@ int fluxattn_last_hip_error(void);
  * Execution setting of every attention launch (forward, fused and joint
  * entry points); the function computed is the one described above.  A
  * launch normally runs one workgroup per 256-query block of each (b,h).
- * When the blocks outnumber G workgroups the grid can instead be G
- * persistent workgroups, each taking an equal contiguous share of the
- * (query block, 64-key tile) pairs in (b, h, query block, key tile) order,
- * so that the last round of blocks no longer leaves compute units idle.
- * A block whose keys fall in two shares is computed in two pieces; each
- * piece leaves its fp32 partial O, row shift and normaliser in a
- * workspace, and the piece finishing second merges the two and stores O.
- * Results then differ from the uncut launch by fp32 summation order only.
- *   groups == 0  (default) G = the device's compute units; cut only when
- *                whole blocks would leave more than 3% of the last round
- *                idle.
- *   groups > 0   G = groups, cut whenever there are more blocks than G.
+ * A cut launch instead runs G persistent workgroups: all but the last one
+ * or two rounds of blocks go whole, in launch order, and the remaining
+ * blocks' (query block, 64-key tile) pairs, in (b, h, query block, key
+ * tile) order, are dealt out as G equal contiguous shares, so that the
+ * last round no longer leaves compute units idle.  A block whose keys fall
+ * in several shares is computed in pieces; each piece leaves its fp32
+ * partial O, row shift and normaliser in a workspace, and the piece
+ * finishing last merges them in share order and stores O.  Results then
+ * differ from the uncut launch by the P roundings (each piece's P is
+ * relative to its own running shift) and fp32 summation order, and are
+ * deterministic.
+ *   groups == 0  (default) G = the device's compute units; cut only with
+ *                at least two rounds of blocks, when whole blocks would
+ *                leave more than 3% of the last round idle.
+ *   groups > 0   G = groups, at most one per key tile of the cut blocks;
+ *                always cut (with more workgroups than blocks, blocks are
+ *                cut into several pieces).
  *   groups < 0   never cut.
  * Process-wide, for launches made after the call.  A cut launch uses a
  * workspace per (device, stream), allocated with hipMalloc by the first
- * such launch on that stream (about 264 KiB per workgroup) and held until
- * the process ends; launches on one stream share it in stream order.
+ * such launch on that stream (128 KiB plus about 264 KiB per workgroup)
+ * and held until the process ends; launches on one stream share it in
+ * stream order, and a launch needing more workgroups than it holds
+ * synchronises the stream once to replace it.
  * Returns FLUXATTN_ERR_INVALID_SHAPE for groups > 16384 (setting unchanged).
  */
 fluxattn_status fluxattn_set_forward_groups(int32_t groups);

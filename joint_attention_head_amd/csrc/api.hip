@@ -157,10 +157,9 @@ bool disjoint(const View &a, const View &b, int64_t B, int64_t H, int64_t N, int
 
 // ---- key-range split of the forward launches
 
-// 0: one workgroup per compute unit, split when there are at least two
-// rounds of query blocks and whole blocks would leave more than 3% of the
-// last round idle; > 0: that many workgroups, split whenever there are more
-// query blocks; < 0: never.
+// 0: one workgroup per compute unit, split where that balances the work
+// (plan_split); > 0: that many workgroups (at most one per tail key tile),
+// always split; < 0: never.
 std::atomic<int32_t> g_forward_groups{0};
 constexpr int32_t kMaxGroups = 1 << 14;
 
@@ -190,9 +189,14 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-size_t split_count_bytes(int32_t groups) { return (static_cast<size_t>(groups) * 4 + 255) & ~size_t(255); }
+// One arrival count per tail block (fewer than 2 * groups of them).  The
+// count region has the size for the largest setting whatever the launch's
+// groups, so that the slots after it never move: launches with different
+// group counts share a workspace, and a slot written by one must not land
+// on counts another expects at zero.
+constexpr size_t kSplitCountBytes = static_cast<size_t>(2) * kMaxGroups * sizeof(int32_t);
 size_t split_bytes(int32_t groups) {
-  return split_count_bytes(groups) + static_cast<size_t>(groups) * 2 * kSplitPieceFloats * sizeof(float);
+  return kSplitCountBytes + static_cast<size_t>(groups) * 2 * kSplitPieceFloats * sizeof(float);
 }
 
 hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
@@ -223,30 +227,40 @@ hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
 }
 
 // Fill a.split_* for a forward launch over nb query blocks of key_tiles
-// tiles each (split_groups stays 0 when the launch is not split).
-hipError_t plan_split(ForwardArgs &a, int64_t nb, hipStream_t s) {
+// key tiles each (split_groups stays 0 when the launch is not split).
+hipError_t plan_split(ForwardArgs &a, int64_t nb, int64_t key_tiles, hipStream_t s) {
   a.split_groups = 0;
   const int32_t setting = g_forward_groups.load(std::memory_order_relaxed);
-  if (setting < 0) return hipSuccess;
+  if (setting < 0 || nb < 1) return hipSuccess;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const int32_t groups = setting > 0 ? setting : compute_units(dev);
-  if (groups < 2 || nb <= groups) return hipSuccess;
+  int64_t groups = setting > 0 ? setting : compute_units(dev);
   if (setting == 0) {
-    // default: only where whole rounds precede the tail (with fewer blocks
-    // the shares would desynchronise all key streaming) and the last round
-    // of whole blocks would leave more than 3% of the compute units idle
-    if (nb < 2 * static_cast<int64_t>(groups)) return hipSuccess;
-    const int64_t rounds = (nb + groups - 1) / groups;
-    if (nb * 100 >= rounds * groups * 97) return hipSuccess;
+    if (nb >= 2 * groups) {
+      // whole rounds, then a tail: split when whole blocks would leave
+      // more than 3% of the last round idle
+      const int64_t rounds = (nb + groups - 1) / groups;
+      if (nb * 100 >= rounds * groups * 97) return hipSuccess;
+    } else {
+      // fewer than two rounds: measured slower cut than whole (at one to two
+      // rounds the shares stream keys out of step; with fewer blocks than
+      // compute units the per-job start-up and the merges outweigh the idle
+      // units: N = 1536 runs 19% (bf16) and 26% (fp8) slower cut)
+      return hipSuccess;
+    }
   }
+  // every share holds at least one pair of the tail (the merge reads a
+  // slot of every share between a block's first and last)
+  const int64_t tail = nb >= 2 * groups ? nb - (nb / groups - 1) * groups : nb;
+  groups = std::min<int64_t>(groups, tail * key_tiles);
+  if (groups < 2 || (setting == 0 && nb == groups)) return hipSuccess;
   void *p = nullptr;
-  e = workspace_for(dev, s, split_bytes(groups), &p);
+  e = workspace_for(dev, s, split_bytes(static_cast<int32_t>(groups)), &p);
   if (e != hipSuccess) return e;
   a.split_cnt = static_cast<int32_t *>(p);
-  a.split_part = reinterpret_cast<float *>(static_cast<char *>(p) + split_count_bytes(groups));
-  a.split_groups = groups;
+  a.split_part = reinterpret_cast<float *>(static_cast<char *>(p) + kSplitCountBytes);
+  a.split_groups = static_cast<int32_t>(groups);
   return hipSuccess;
 }
 
@@ -456,7 +470,7 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
   }
   const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
                          is_contiguous(o, H, N, D));
-  const hipError_t ps = plan_split(a, forward_grid_blocks(BH, N), static_cast<hipStream_t>(stream));
+  const hipError_t ps = plan_split(a, forward_grid_blocks(BH, N), forward_key_tiles(N), static_cast<hipStream_t>(stream));
   if (ps != hipSuccess) return hip_fail(ps);
   const hipError_t e = FP8 ? launch_forward_fp8(a, fused, strided, static_cast<hipStream_t>(stream))
                            : launch_forward_bf16(a, fused, strided, static_cast<hipStream_t>(stream));

@@ -218,7 +218,7 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
 // the whole head (job.cut < 0: O is stored) or one piece of a split block.
 template <bool FUSEQ, bool STRIDED>
 __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const RopeLds *rope, int *split_ticket,
-                                         const SplitJob &job, const int tid_in, const int group, const int gw) {
+                                         const SplitJob job, const int tid_in, const int group, const int gw) {
   // lane constants are computed per job (an opaque copy of the thread id
   // keeps them from being hoisted out of the job loop, where they would
   // overlap the fused query transform's temporaries)
@@ -227,7 +227,9 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
   const int rank = gw * 64 + lane;             // 0..255 inside the group
-  const int bh = job.bh, qt = job.qt, kt0 = job.kt0, T = job.T;
+  // wave-uniform job fields (they address the scalar buffer descriptors)
+  const int bh = __builtin_amdgcn_readfirstlane(job.bh), qt = __builtin_amdgcn_readfirstlane(job.qt);
+  const int kt0 = __builtin_amdgcn_readfirstlane(job.kt0), T = __builtin_amdgcn_readfirstlane(job.T);
 
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 1, bh, a.H, N);
   const HeadView vk = head_view<STRIDED>(a.k, a.sk, 1, bh, a.H, N);

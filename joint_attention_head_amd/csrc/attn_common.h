@@ -89,27 +89,36 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int total) {
 
 // ---- Key-range split.  Without a split, workgroup w computes query block
 // w whole (blocks in (b*h, query tile) order).  With split_groups = G
-// persistent workgroups and nb blocks (the host splits only when nb > G),
-// the first F = nb / G - 1 rounds go as whole blocks in launch order:
-// workgroup w takes blocks w, w + G, ..., so the workgroups running at one
-// time work on neighbouring blocks of the same heads and stream the same
-// key tiles in step, sharing them in L2.  The remaining nb - F G blocks
-// (between G and 2G - 1) form the tail: its (query block, key tile) pairs,
-// key tiles in order inside each block, are dealt out as G equal contiguous
-// shares, workgroup w taking share w.  Every share spans at least one
-// block's key tiles, so a tail block is cut at most once, between the
-// shares of workgroups w - 1 and w for cut index w.
+// persistent workgroups and nb blocks, the first F = max(nb / G - 1, 0)
+// rounds go as whole blocks in launch order: workgroup w takes blocks w,
+// w + G, ..., so the workgroups running at one time work on neighbouring
+// blocks of the same heads and stream the same key tiles in step, sharing
+// them in L2.  The remaining blocks form the tail (fewer than 2G): its
+// (query block, key tile) pairs, key tiles in order inside each block, are
+// dealt out as G equal contiguous shares, share w = pairs
+// [U w / G, U (w + 1) / G) of the tail's U to workgroup w.  A share spans
+// at most two tail blocks when it is shorter than a block, and then cuts
+// blocks into two or more pieces; a longer share has at most a partial
+// block at each end.  A partial piece goes to slot 2w if it is the first
+// job of share w, else 2w + 1.
 struct SplitRange {
   int whole;          // whole blocks still to do before the tail
   int blk, stride;    // next whole block, and the step between them
   int64_t u, end;     // next pair of the tail share, end of the share
-  int key_tiles, q_tiles, logical;
+  int64_t start;      // first pair of the share
+  int64_t U;          // pairs in the tail
+  int base;           // first tail block
+  int key_tiles, q_tiles, logical, groups;
 };
 struct SplitJob {
   int bh, qt;         // head and query block
   int kt0, T;         // key tiles [kt0, kt0 + T)
-  int cut;            // -1: the whole block; else the index of its cut
-  int piece;          // 0: keys before the cut, 1: after
+  int cut;            // -1: the whole block; else its index in the tail
+  int slot;           // partial slot of this piece
+  int w_lo, w_hi;     // shares that hold pieces of the block
+  int64_t U;          // tail pairs, key tiles per block and groups: what
+  int key_tiles;      // the merge needs to find the other pieces' slots
+  int groups;
 };
 
 __device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows, int keys, int logical) {
@@ -118,19 +127,22 @@ __device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows
   r.key_tiles = (a.N + keys - 1) / keys;
   r.logical = logical;
   r.blk = logical;
+  r.groups = a.split_groups;
   if (a.split_groups > 0) {
     const int G = a.split_groups;
     const int nb = a.BH * r.q_tiles;
-    r.whole = nb / G - 1;
+    r.whole = max(nb / G - 1, 0);
     r.stride = G;
-    const int64_t base = (int64_t)r.whole * G * r.key_tiles;
-    const int64_t U = (int64_t)(nb - r.whole * G) * r.key_tiles;
-    r.u = base + U * logical / G;
-    r.end = base + U * (logical + 1) / G;
+    r.base = r.whole * G;
+    r.U = (int64_t)(nb - r.base) * r.key_tiles;
+    r.start = r.U * logical / G;
+    r.u = r.start;
+    r.end = r.U * (logical + 1) / G;
   } else {
     r.whole = 1;
     r.stride = 0;
-    r.u = r.end = 0;
+    r.base = 0;
+    r.U = r.start = r.u = r.end = 0;
   }
   return r;
 }
@@ -150,15 +162,33 @@ __device__ __forceinline__ SplitRange split_range_load(const SplitRange *p) {
   r.stride = u32(p->stride);
   r.u = u64(p->u);
   r.end = u64(p->end);
+  r.start = u64(p->start);
+  r.U = u64(p->U);
+  r.base = u32(p->base);
   r.key_tiles = u32(p->key_tiles);
   r.q_tiles = u32(p->q_tiles);
   r.logical = u32(p->logical);
+  r.groups = u32(p->groups);
   return r;
+}
+
+// Share of tail pair u: the largest w with U w / G <= u.
+__device__ __forceinline__ int split_share_of(int64_t u, int64_t U, int G) { return (int)(((u + 1) * G - 1) / U); }
+
+// Partial slot of share w's piece of tail block b: its first job when the
+// share starts inside or at the start of the block, else its last.
+__device__ __forceinline__ int split_slot(int w, int b, int64_t U, int key_tiles, int G) {
+  return U * w / G >= (int64_t)b * key_tiles ? 2 * w : 2 * w + 1;
 }
 
 // Next job of the workgroup (false when it is done).
 __device__ __forceinline__ bool split_next(SplitRange &r, SplitJob &j) {
   int blk;
+  j.cut = -1;
+  j.slot = j.w_lo = j.w_hi = 0;
+  j.U = r.U;
+  j.key_tiles = r.key_tiles;
+  j.groups = r.groups;
   if (r.whole > 0) {
     blk = r.blk;
     r.blk += r.stride;
@@ -167,28 +197,33 @@ __device__ __forceinline__ bool split_next(SplitRange &r, SplitJob &j) {
     j.T = r.key_tiles;
   } else {
     if (r.u >= r.end) return false;
-    blk = (int)(r.u / r.key_tiles);
-    j.kt0 = (int)(r.u - (int64_t)blk * r.key_tiles);
+    const int b = (int)(r.u / r.key_tiles);
+    j.kt0 = (int)(r.u - (int64_t)b * r.key_tiles);
     j.T = (int)min((int64_t)(r.key_tiles - j.kt0), r.end - r.u);
     r.u += j.T;
+    blk = r.base + b;
+    if (j.T != r.key_tiles) {
+      j.cut = b;
+      j.slot = r.start >= (int64_t)b * r.key_tiles ? 2 * r.logical : 2 * r.logical + 1;
+      j.w_lo = split_share_of((int64_t)b * r.key_tiles, r.U, r.groups);
+      j.w_hi = split_share_of((int64_t)(b + 1) * r.key_tiles - 1, r.U, r.groups);
+    }
   }
   j.bh = blk / r.q_tiles;
   j.qt = blk - j.bh * r.q_tiles;
-  j.piece = j.kt0 == 0 ? 0 : 1;
-  j.cut = j.T == r.key_tiles ? -1 : (j.piece == 0 ? r.logical + 1 : r.logical);
   return true;
 }
 
-// End of one piece of a split block.  The piece stores its O accumulators
+// End of one piece of a cut block.  The piece stores its O accumulators
 // o (unnormalised, relative to 2^b: row shift b in base-2 units) and its
-// normaliser l, then counts itself in at the cut.  The first to arrive
-// returns false; the second reads the other piece and merges it into
-// (o, b, l), rescaling both to the larger shift, resets the count for the
-// next launch and returns true (it then stores O).  Nobody waits: the
-// merge happens in whichever order the pieces finish, and it is symmetric
-// in the two pieces, so the result does not depend on that order.
-// Coherence between the two workgroups (possibly on different XCDs, whose
-// L2 caches are not coherent with each other) comes from device-scope
+// normaliser l in its slot, then counts itself in at the block.  All but
+// the last to arrive return false; the last reads the other pieces and
+// merges them into (o, b, l): every piece rescaled to the largest shift
+// and summed in share order (whichever piece merges, the result is the
+// same, bit for bit), resets the count for the next launch and returns
+// true (it then stores O).  Nobody waits for anybody.
+// Coherence between the workgroups (possibly on different XCDs, whose L2
+// caches are not coherent with each other) comes from device-scope
 // accesses to the partials and the count alone: the partial stores and
 // loads carry the device-scope cache policy (sc1), the stores are retired
 // (vmcnt 0) before the workgroup barrier that precedes the count, and the
@@ -200,49 +235,75 @@ constexpr int kCPolDevice = 16;   // buffer cache policy: sc1 (device scope)
 __device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob &job, f32x16_t (&o)[4], float &b,
                                             float &l, int tid, int *ticket) {
   constexpr uint32_t kPieceBytes = (uint32_t)(kSplitPieceFloats * 4);
-  const __amdgpu_buffer_rsrc_t mine =
-      make_rsrc(a.split_part + ((int64_t)job.cut * 2 + job.piece) * kSplitPieceFloats, kPieceBytes);
-  const __amdgpu_buffer_rsrc_t other =
-      make_rsrc(a.split_part + ((int64_t)job.cut * 2 + (job.piece ^ 1)) * kSplitPieceFloats, kPieceBytes);
+  constexpr uint32_t kBLOffset = 64u * 4u * kSplitThreads;
+  auto slot_rsrc = [&](int slot) {
+    return make_rsrc(a.split_part + (int64_t)slot * kSplitPieceFloats, kPieceBytes);
+  };
   const uint32_t t16 = (uint32_t)tid * 16u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int db = i >> 2, g = i & 3;
-    u32x4_t w;
-    w[0] = __float_as_uint(o[db][4 * g + 0]);
-    w[1] = __float_as_uint(o[db][4 * g + 1]);
-    w[2] = __float_as_uint(o[db][4 * g + 2]);
-    w[3] = __float_as_uint(o[db][4 * g + 3]);
-    __builtin_amdgcn_raw_buffer_store_b128(w, mine, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
-  }
   {
+    const __amdgpu_buffer_rsrc_t mine = slot_rsrc(job.slot);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int db = i >> 2, g = i & 3;
+      u32x4_t w;
+      w[0] = __float_as_uint(o[db][4 * g + 0]);
+      w[1] = __float_as_uint(o[db][4 * g + 1]);
+      w[2] = __float_as_uint(o[db][4 * g + 2]);
+      w[3] = __float_as_uint(o[db][4 * g + 3]);
+      __builtin_amdgcn_raw_buffer_store_b128(w, mine, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
+    }
     u32x2_t w;
     w[0] = __float_as_uint(b);
     w[1] = __float_as_uint(l);
-    __builtin_amdgcn_raw_buffer_store_b64(w, mine, 64u * 4u * kSplitThreads + (uint32_t)tid * 8u, 0, kCPolDevice);
+    __builtin_amdgcn_raw_buffer_store_b64(w, mine, kBLOffset + (uint32_t)tid * 8u, 0, kCPolDevice);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) *ticket = __hip_atomic_fetch_add(a.split_cnt + job.cut, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (*ticket == 0) return false;
+  if (*ticket != job.w_hi - job.w_lo) return false;
   if (tid == 0) __hip_atomic_store(a.split_cnt + job.cut, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(other, 64u * 4u * kSplitThreads + (uint32_t)tid * 8u, 0,
-                                                           kCPolDevice);
-  u32x4_t x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    x[i] = __builtin_amdgcn_raw_buffer_load_b128(other, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
-  const float b2 = __uint_as_float(blw[0]), l2 = __uint_as_float(blw[1]);
-  const float m = fmaxf(b, b2);
-  const float sa = __builtin_amdgcn_exp2f(b - m), sb = __builtin_amdgcn_exp2f(b2 - m);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int db = i >> 2, g = i & 3;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[db][4 * g + e] = o[db][4 * g + e] * sa + __uint_as_float(x[i][e]) * sb;
+  const int own = job.slot >> 1;
+  // the largest row shift over the pieces
+  float m = b;
+  for (int w = job.w_lo; w <= job.w_hi; ++w) {
+    if (w == own) continue;
+    const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(
+        slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups)), kBLOffset + (uint32_t)tid * 8u, 0,
+        kCPolDevice);
+    m = fmaxf(m, __uint_as_float(blw[0]));
   }
-  l = l * sa + l2 * sb;
+  // sum in share order
+  f32x16_t acc[4];
+  float lacc = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16_t{};
+  for (int w = job.w_lo; w <= job.w_hi; ++w) {
+    if (w == own) {
+      const float sc = __builtin_amdgcn_exp2f(b - m);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = fmaf(o[db][e], sc, acc[db][e]);
+      lacc = fmaf(l, sc, lacc);
+    } else {
+      const __amdgpu_buffer_rsrc_t other = slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups));
+      const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(other, kBLOffset + (uint32_t)tid * 8u, 0, kCPolDevice);
+      const float sc = __builtin_amdgcn_exp2f(__uint_as_float(blw[0]) - m);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int db = i >> 2, g = i & 3;
+        const u32x4_t x =
+            __builtin_amdgcn_raw_buffer_load_b128(other, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * g + e] = fmaf(__uint_as_float(x[e]), sc, acc[db][4 * g + e]);
+      }
+      lacc = fmaf(__uint_as_float(blw[1]), sc, lacc);
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = acc[db];
+  l = lacc;
   b = m;
   return true;
 }

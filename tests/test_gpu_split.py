@@ -33,7 +33,9 @@ FP8_TOL = (4e-2, 4e-3)
 # (B, H, text tokens, image grid): N = 1000 (8 query blocks, 16 key tiles,
 # the last one 40 keys) and N = 667 (18 blocks, 11 tiles, the last 27 keys)
 SHAPES = {"n1000": (1, 2, 40, (24, 40)), "n667": (2, 3, 7, (20, 33))}
-GROUPS = (2, 3, 5, 7)
+# up to 7: whole rounds and a tail cut at most once per block; 12 and more:
+# more workgroups than blocks, blocks cut into up to five pieces
+GROUPS = (2, 3, 5, 7, 12, 20, 31)
 
 
 def _flush(msg):
@@ -133,7 +135,6 @@ PATHS = {
 def test_split_matches_oracle_and_uncut_launch(path, shape):
     run, ref_fn, dtype, tol = PATHS[path]
     inp = inputs(shape, dtype)
-    assert n_blocks(inp) > max(GROUPS)
     ref = ref_fn(inp)
     with forward_groups(-1):
         whole = run(inp)
@@ -214,3 +215,40 @@ def test_split_on_two_streams_at_once():
         assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
         assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
     check_close(f64(ref_b), attention_ref(b), BF16_TOL, "split, second stream's inputs")
+
+
+def test_split_many_pieces_flux_dev_512():
+    """FLUX-dev 512x512 (B=1, H=24, N=1536: 144 query blocks of 24 key
+    tiles) over 256 workgroups: more workgroups than blocks, every block cut
+    into two or three pieces (shares of 13.5 tiles); close to the uncut
+    launch, and the oracle on sampled rows of two heads.  (The default
+    setting leaves this size uncut: measured faster.)"""
+    inp = make_inputs(custom_workload(1, 24, 512, (32, 32)))
+    with forward_groups(256):
+        o = forward_bf16(inp)
+    with forward_groups(-1):
+        whole = forward_bf16(inp)
+    torch.cuda.synchronize()
+    close_to_uncut(o, whole, "bf16", "256 workgroups N=1536")
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(1500, 1536), np.arange(0, 1536, 37)]))
+    for h in (0, 23):
+        sl = (slice(0, 1), slice(h, h + 1))
+        ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
+        check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"256 workgroups N=1536 head {h}")
+
+
+def test_split_workspace_shared_across_group_counts():
+    """Launches with different group counts share one stream's workspace:
+    a small count's partial slots must not land on the arrival counts a
+    larger count expects at zero (G = 100 needs 200 counts, G = 5 ten).
+    G = 100 also cuts each of the 8 blocks into about a dozen pieces."""
+    inp = inputs("n1000")
+    with forward_groups(-1):
+        whole = forward_bf16(inp)
+    ref = attention_ref(inp)
+    for g in (100, 5, 100, 5):
+        with forward_groups(g):
+            o = forward_bf16(inp)
+        torch.cuda.synchronize()
+        check_close(f64(o), ref, BF16_TOL, f"shared workspace G={g}")
+        close_to_uncut(o, whole, "bf16", f"shared workspace G={g}")
