@@ -374,6 +374,18 @@ fluxattn_status fluxattn_set_forward_groups(int32_t groups);
 /* The current setting of fluxattn_set_forward_groups. */
 int32_t fluxattn_get_forward_groups(void);
 
+/*
+ * Frees every split workspace the library holds (see
+ * fluxattn_set_forward_groups), on every device, after waiting for each
+ * such device to finish its work (hipDeviceSynchronize: a workspace's
+ * stream may no longer exist).  The next cut launch on a stream allocates
+ * again.  Must not run concurrently with attention launches.  With no
+ * workspace held it touches no device and returns FLUXATTN_OK; on a HIP
+ * error it keeps the workspaces it could not free and returns
+ * FLUXATTN_ERR_HIP.
+ */
+fluxattn_status fluxattn_release_workspaces(void);
+
 /* Library version as 10000*major + 100*minor + patch. */
 int fluxattn_version(void);
 

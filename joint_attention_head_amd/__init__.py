@@ -65,6 +65,7 @@ EXPORTS = (
     "fluxattn_last_hip_error",
     "fluxattn_set_forward_groups",
     "fluxattn_get_forward_groups",
+    "fluxattn_release_workspaces",
     "fluxattn_version",
 )
 
@@ -125,6 +126,7 @@ _SIGS = {
                                         _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _p],
     "fluxattn_set_forward_groups": [_i32],
     "fluxattn_get_forward_groups": [],
+    "fluxattn_release_workspaces": [],
 }
 
 
@@ -395,6 +397,11 @@ def fluxattn_set_forward_groups(groups: int):
 
 def fluxattn_get_forward_groups() -> int:
     return int(lib().fluxattn_get_forward_groups())
+
+
+def fluxattn_release_workspaces():
+    """Free the split workspaces (after synchronising their devices)."""
+    _check(lib().fluxattn_release_workspaces())
 
 
 def layout_of(t: torch.Tensor) -> Layout:

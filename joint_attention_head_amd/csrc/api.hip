@@ -718,6 +718,28 @@ fluxattn_status fluxattn_set_forward_groups(int32_t groups) {
 
 int32_t fluxattn_get_forward_groups(void) { return g_forward_groups.load(std::memory_order_relaxed); }
 
+fluxattn_status fluxattn_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (g_ws.empty()) return FLUXATTN_OK;
+  int prev = 0;
+  hipError_t first = hipGetDevice(&prev);
+  if (first != hipSuccess) return hip_fail(first);
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    hipError_t e = hipSetDevice(it->first.first);
+    if (e == hipSuccess) e = hipDeviceSynchronize();   // its stream may be gone: wait for the device
+    if (e == hipSuccess && it->second.p) e = hipFree(it->second.p);
+    if (e != hipSuccess) {
+      if (first == hipSuccess) first = e;
+      ++it;   // keep what could not be freed
+      continue;
+    }
+    it = g_ws.erase(it);
+  }
+  const hipError_t r = hipSetDevice(prev);
+  if (first == hipSuccess) first = r;
+  return first == hipSuccess ? FLUXATTN_OK : hip_fail(first);
+}
+
 int fluxattn_version(void) { return 130; }
 
 }  // extern "C"

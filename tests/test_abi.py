@@ -110,6 +110,14 @@ def test_forward_groups_setting(lib):
         lib.fluxattn_set_forward_groups(0)
 
 
+def test_release_workspaces_without_any_is_a_no_op(lib):
+    """Without a GPU no split launch can have run: nothing to free, so it
+    returns OK without touching a device (with workspaces held it would
+    free them)."""
+    assert lib.fluxattn_release_workspaces() == OK
+    assert lib.fluxattn_last_hip_error() == 0
+
+
 def test_null_pointers(lib):
     for kw in ("q", "k", "qo", "ko", "wq", "wk", "pos"):
         assert prologue(lib, **{kw: None}) == NULLP, kw

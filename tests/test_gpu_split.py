@@ -252,3 +252,18 @@ def test_split_workspace_shared_across_group_counts():
         torch.cuda.synchronize()
         check_close(f64(o), ref, BF16_TOL, f"shared workspace G={g}")
         close_to_uncut(o, whole, "bf16", f"shared workspace G={g}")
+
+
+def test_release_workspaces_then_cut_again():
+    """After the workspaces are freed, the next cut launch allocates a fresh
+    one and is right."""
+    inp = inputs("n667")
+    ref = attention_ref(inp)
+    with forward_groups(5):
+        o1 = forward_bf16(inp)
+        torch.cuda.synchronize()
+        fa.fluxattn_release_workspaces()
+        o2 = forward_bf16(inp)
+    torch.cuda.synchronize()
+    check_close(f64(o2), ref, BF16_TOL, "cut after release")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
