@@ -51,8 +51,8 @@
 //  * A workgroup runs a list of jobs (attn_common.h): normally one whole
 //    query block; when the host balances the last round, a persistent grid
 //    takes whole blocks in launch order and then an equal share of the
-//    tail's (query block, key tile) pairs, a cut block's two pieces being
-//    merged by whichever finishes second.
+//    tail's (query block, key tile) pairs, a cut block's pieces being
+//    merged by whichever finishes last.
 // FP8 inputs run on the fp8 matrix cores instead (attention_fp8.hip).
 #include "attn_common.h"
 

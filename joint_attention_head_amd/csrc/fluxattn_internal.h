@@ -65,11 +65,11 @@ struct ForwardArgs {
   // (the key prologue's frequencies, in revolutions)
   float rope_rate[3][kPairs];
   // Key-range split (split_groups > 0): a persistent grid of split_groups
-  // workgroups, each taking an equal contiguous share of the
-  // (query block, key tile) pairs.  A query block cut between two
-  // workgroups leaves one partial result per piece in split_part; the
-  // second piece to finish merges them (split_cnt holds the arrival count
-  // of each cut and is left at zero).
+  // workgroups, whole blocks first, then an equal contiguous share each of
+  // the remaining (query block, key tile) pairs.  A query block cut between
+  // workgroups leaves one partial result per piece in split_part; the last
+  // piece to finish merges them (split_cnt holds the arrival count of each
+  // cut block and is left at zero).
   float *split_part;
   int32_t *split_cnt;
   int32_t split_groups;
@@ -78,7 +78,8 @@ struct ForwardArgs {
 // Partial result of one piece of a split query block: per thread of the
 // 512-thread workgroup, 64 fp32 O accumulators (16 float4, stored
 // [float4 index][thread]) then the row shift b and normaliser l (float2
-// per thread).  Two pieces per cut.
+// per thread).  Two slots per workgroup: the first and the last job of its
+// share.
 constexpr int kSplitThreads = 512;
 constexpr int64_t kSplitPieceFloats = (int64_t)kSplitThreads * 64 + (int64_t)kSplitThreads * 2;
 

@@ -1,11 +1,11 @@
 """Key-range split of the attention launches, through the C ABI.
 
 With G persistent workgroups each taking an equal share of the (query
-block, key tile) pairs, a query block can be computed in two key ranges
-whose partial results the second piece to finish merges.  The split is
-forced here at sizes the fp64 oracle handles by setting G below the number
-of 256-query blocks; every case spans several 64-key tiles, with a ragged
-last key tile and a ragged last query block.  Checked: parity with the
+block, key tile) pairs, a query block can be computed in several key
+ranges whose partial results the last piece to finish merges.  The split
+is forced here at sizes the fp64 oracle handles by setting G below or
+above the number of 256-query blocks; every case spans several 64-key
+tiles, with a ragged last key tile and a ragged last query block.  Checked: parity with the
 oracle (same tolerances as the uncut launch), closeness to the uncut launch
 (a piece that starts inside a block takes its first row shift from its own
 first tile, so its P values are rounded relative to another shift: the two
