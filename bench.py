@@ -11,9 +11,15 @@ runs the prologue on both and the plain attention kernel.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 
+The attention launches use the key-range split with a workspace allocated
+(zeroed) before the timed region (--groups, default 0: the library's rule).
+
 Prints one JSON line: TFLOP/s of the step (4*B*H*N^2*d per step), the
-attention kernel's roofline fraction (its own average launch time from HIP
-events on the launch stream), the same figures at N=4608 (FLUX-dev 1024x1024)
+attention kernel's roofline fraction (its own mean launch time from HIP
+events on the launch stream; median and minimum beside it), the sustained
+graphics clock and power over a second of back-to-back launches (amdsmi),
+the prologue's GB/s warm and with the MALL flushed before every launch,
+the same figures at N=4608 (FLUX-dev 1024x1024)
 under "also", the fp8 path (E4M3 Q/K/V, fp8 matrix cores) on the 2048x2048
 image-to-image workload (B=1, H=24, N = 512 + 2 x 128x128 = 33280) under
 "fp8" with its roofline against the fp8 MFMA peak, every workload's forward
@@ -121,17 +127,104 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-all-configs", dest="all_configs", action="store_false",
                    help="skip the per-workload table (every workload's forward TFLOP/s and MFMA fraction)")
+    p.add_argument("--no-clock", dest="clock", action="store_false",
+                   help="skip the sustained-clock sample (one second of attention launches per kernel)")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--path", choices=("fused", "unfused"), default="fused")
     p.add_argument("--groups", type=int, default=0,
-                   help="attention workgroup setting: 0 = one per compute unit, key ranges split where that "
-                        "balances the last round (default); < 0 = never split; > 0 = that many workgroups")
+                   help="key-range split of the attention launches: 0 = one workgroup per compute unit, "
+                        "cut where that balances the last round (default); < 0 = never cut; "
+                        "> 0 = that many workgroups")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
 
 
-def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
+def stats(xs):
+    """mean, median and minimum of a list of seconds."""
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return sum(ys) / n, med, ys[0]
+
+
+class ClockSampler:
+    """Graphics clock and socket power of GPU 0 through amdsmi (None where
+    the library or the query is not available)."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            self.h = None
+
+    def read(self):
+        if self.h is None:
+            return None, None
+        clk = power = None
+        try:
+            clk = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.SYS)["clk"]
+        except Exception:
+            pass
+        try:
+            info = self.amdsmi.amdsmi_get_power_info(self.h)
+            power = info.get("current_socket_power") or info.get("average_socket_power")
+        except Exception:
+            pass
+        return clk, power
+
+    def during(self, fn, seconds=1.0):
+        """Run fn() back to back for about `seconds` while sampling every
+        10 ms; median clock (MHz) and power (W) of the samples taken after
+        the first quarter (the clock settles under load)."""
+        import threading
+
+        import torch
+        if self.h is None:
+            return None
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                samples.append((time.perf_counter(), *self.read()))
+                time.sleep(0.01)
+
+        th = threading.Thread(target=poll, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+            n += 8
+        stop.set()
+        th.join()
+        t1 = time.perf_counter()
+        late = [s for s in samples if s[0] >= t0 + 0.25 * (t1 - t0)]
+        clk = sorted(c for _, c, _ in late if c)
+        pw = sorted(p for _, _, p in late if p)
+        if not clk:
+            return None
+        return {"clock_MHz": clk[len(clk) // 2], "power_W": pw[len(pw) // 2] if pw else None,
+                "samples": len(late), "launches": n, "seconds": round(t1 - t0, 2)}
+
+
+_CLOCK = None
+
+
+def clock_sampler():
+    global _CLOCK
+    if _CLOCK is None:
+        _CLOCK = ClockSampler()
+    return _CLOCK
+
+
+def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int = 0, clock: bool = False):
     import torch
 
     import joint_attention_head_amd as fa
@@ -148,6 +241,8 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
     if fp8:
         sq, sk, sv = (t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale))
         sqn, skn = torch.empty_like(sq), torch.empty_like(sk)
+    # the split workspace (zeroed once, outside the timed region)
+    ws = fa.split_workspace(w.B, w.H, w.N, groups, device=dev) if groups >= 0 else None
     stream = torch.cuda.current_stream()
 
     def prologue():
@@ -163,13 +258,13 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
 
     def attention():
         if fp8 and path == "fused":
-            fa.fluxattn_forward_fused_fp8(q, kn, v, sq, skn, sv, w_q, pos, o=o, stream=stream)
+            fa.fluxattn_forward_fused_ex_fp8(q, kn, v, sq, skn, sv, w_q, pos, o=o, split=ws, stream=stream)
         elif fp8:
-            fa.fluxattn_forward_fp8(qn, kn, v, sqn, skn, sv, o=o, stream=stream)
+            fa.fluxattn_forward_ex_fp8(qn, kn, v, sqn, skn, sv, o=o, split=ws, stream=stream)
         elif path == "fused":
-            fa.fluxattn_forward_fused_bf16(q, kn, v, w_q, pos, o=o, stream=stream)
+            fa.fluxattn_forward_fused_ex_bf16(q, kn, v, w_q, pos, o=o, split=ws, stream=stream)
         else:
-            fa.fluxattn_forward_bf16(qn, kn, v, o=o, stream=stream)
+            fa.fluxattn_forward_ex_bf16(qn, kn, v, o=o, split=ws, stream=stream)
 
     def step(ev=None):
         if ev is not None:
@@ -193,28 +288,49 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused"):
     wall = time.perf_counter() - t0
     pro = [e[0].elapsed_time(e[1]) * 1e-3 for e in evs]
     fwd = [e[1].elapsed_time(e[2]) * 1e-3 for e in evs]
-    span = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3
     assert torch.isfinite(o).all().item()
+    if ws is not None and ws.nbytes:
+        assert not ws.counts().any().item(), "split arrival counts left non-zero"
+    # the prologue with the 256 MB MALL flushed before every launch: a
+    # 512 MiB fill between launches, outside the events
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(steps):
+        scratch.fill_(i & 0xFF)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        prologue()
+        e[1].record(stream)
+        cold.append(e)
+    torch.cuda.synchronize()
+    pro_cold = [e[0].elapsed_time(e[1]) * 1e-3 for e in cold]
+    del scratch
+    sustained = clock_sampler().during(attention) if clock else None
     flops = w.flops
     # read + write K (fused path) or Q and K
     esize = 1 if fp8 else 2
     prologue_bytes = (2.0 if path == "fused" else 4.0) * w.B * w.H * w.N * 128 * esize
-    attn_min_bytes = w.B * w.H * w.N * 128 * (3.0 * esize + 2)   # read Q, K, V, write bf16 O once
-    t_fwd = sum(fwd) / len(fwd)
-    t_pro = sum(pro) / len(pro)
+    t_fwd, t_fwd_med, t_fwd_min = stats(fwd)
+    t_pro, t_pro_med, t_pro_min = stats(pro)
+    t_cold, t_cold_med, _ = stats(pro_cold)
     res = {
         "workload": w,
         "ms_per_step": wall / steps * 1e3,
-        "gpu_span_ms_per_step": span / steps * 1e3,
         "value": flops / (wall / steps) / 1e12,
         "forward_ms": t_fwd * 1e3,
+        "forward_ms_median": t_fwd_med * 1e3,
+        "forward_ms_min": t_fwd_min * 1e3,
         "forward_tflops": flops / t_fwd / 1e12,
         "prologue_us": t_pro * 1e6,
-        "prologue_gbs": prologue_bytes / t_pro / 1e9,
-        "attn_min_bytes": attn_min_bytes,
+        "prologue_us_median": t_pro_med * 1e6,
+        "prologue_gbs": prologue_bytes / t_pro_med / 1e9,
+        "prologue_gbs_mall_flushed": prologue_bytes / t_cold_med / 1e9,
+        "prologue_bytes": prologue_bytes,
         "flops": flops,
+        "split_workspace_bytes": ws.nbytes if ws is not None else 0,
+        "sustained": sustained,
     }
-    del q, k, v, qn, kn, o
+    del q, k, v, qn, kn, o, ws
     if fp8:
         del sq, sk, sv, sqn, skn
     torch.cuda.empty_cache()
@@ -232,7 +348,18 @@ def calibrate_copy():
     print(f"copy calibration: torch.neg over {n * 2} bytes read and {n * 2} written", file=sys.stderr)
 
 
-def cpu_baseline(name: str, n_heads: int):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(name: str, n_heads: int, gpu_forward_s: float):
     import numpy as np
 
     import oracle
@@ -254,15 +381,38 @@ def cpu_baseline(name: str, n_heads: int):
         assert np.isfinite(out).all()
     dt = time.perf_counter() - t0
     flops = 4.0 * len(heads) * w.N * w.N * 128
+    full = dt * (w.B * w.H) / len(heads)
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{len(heads)} of {w.B * w.H} (b,h) heads of {name} (N={w.N}), all query rows, "
-                  f"prologue + attention in fp64 NumPy; {dt:.1f} s",
+                  f"prologue + attention in fp64 NumPy with {threads} BLAS threads; {dt:.1f} s",
         "seconds": round(dt, 2),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "full_workload_seconds_extrapolated": round(full, 1),
+        "gpu_forward_over_cpu": round(full / gpu_forward_s, 1),
     }
+
+
+def roofline(r, kind, args, peak, kernel):
+    out = {
+        "kernel": kernel,
+        "bound": "mfma",
+        "achieved": round(r["forward_tflops"], 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(r["forward_tflops"] / peak, 4),
+        "traffic": measured_traffic(args.path, kind),
+        "launch_ms": round(r["forward_ms"], 4),
+        "launch_ms_median": round(r["forward_ms_median"], 4),
+        "launch_ms_min": round(r["forward_ms_min"], 4),
+        "counters": measured_mfma_busy(kind) if args.path == "fused" else None,
+        "sustained": r["sustained"],
+    }
+    return out
 
 
 def main():
@@ -275,16 +425,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
-    import joint_attention_head_amd as fa
-    fa.fluxattn_set_forward_groups(args.groups)
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup} groups={args.groups}",
           file=sys.stderr, flush=True)
-    main_res = run_gpu(args.workload, args.steps, args.warmup, args.path)
+    main_res = run_gpu(args.workload, args.steps, args.warmup, args.path, args.groups, args.clock)
     done = {args.workload: main_res}
-    print(f"bench: {args.workload} forward {main_res['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+    print(f"bench: {args.workload} forward mean {main_res['forward_ms']:.4f} ms median "
+          f"{main_res['forward_ms_median']:.4f} min {main_res['forward_ms_min']:.4f}; sustained "
+          f"{main_res['sustained']}", file=sys.stderr, flush=True)
     also = None
     if args.also:
-        r = run_gpu(args.also, args.steps, args.warmup, args.path)
+        r = run_gpu(args.also, args.steps, args.warmup, args.path, args.groups)
         done[args.also] = r
         w = r["workload"]
         also = {
@@ -293,12 +443,15 @@ def main():
             "ms_per_step": round(r["ms_per_step"], 4),
             "forward_tflops": round(r["forward_tflops"], 2),
             "forward_frac_of_bf16_peak": round(r["forward_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "forward_ms_median": round(r["forward_ms_median"], 4),
+            "forward_ms_min": round(r["forward_ms_min"], 4),
             "prologue_gbs": round(r["prologue_gbs"], 1),
+            "prologue_gbs_mall_flushed": round(r["prologue_gbs_mall_flushed"], 1),
         }
-        print(f"bench: {args.also} forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+        print(f"bench: {args.also} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
     fp8 = None
     if args.fp8:
-        r = run_gpu(args.fp8, args.steps, args.warmup, args.path)
+        r = run_gpu(args.fp8, args.steps, args.warmup, args.path, args.groups, args.clock)
         done[args.fp8] = r
         w = r["workload"]
         fp8 = {
@@ -309,21 +462,22 @@ def main():
             "unit": "TFLOP/s",
             "ms_per_step": round(r["ms_per_step"], 4),
             "dtype": "fp8-e4m3",
-            "roofline": {
-                "kernel": "attn_fwd_fp8_kernel (E4M3 MFMA, %s)" % (
-                    "fused query prologue" if args.path == "fused" else "plain"),
-                "bound": "mfma",
-                "achieved": round(r["forward_tflops"], 2),
-                "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": round(r["forward_tflops"] / FP8_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.path, "fp8"),
-                "launch_ms": round(r["forward_ms"], 4),
-                "counters": measured_mfma_busy("fp8") if args.path == "fused" else None,
+            "roofline": roofline(r, "fp8", args, FP8_PEAK_TFLOPS, "attn_fwd_fp8_kernel (E4M3 MFMA, %s)" % (
+                "fused query prologue" if args.path == "fused" else "plain")),
+            "prologue": {
+                "kernel": "prologue_fp8_kernel (%s)" % ("keys only" if args.path == "fused" else "queries and keys"),
+                "bound": "hbm",
+                "achieved": round(r["prologue_gbs"], 1),
+                "achieved_mall_flushed": round(r["prologue_gbs_mall_flushed"], 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(r["prologue_gbs"] / HBM_PEAK_GBS, 4),
+                "launch_us_median": round(r["prologue_us_median"], 2),
             },
-            "prologue_gbs": round(r["prologue_gbs"], 1),
+            "split_workspace_bytes": r["split_workspace_bytes"],
         }
-        print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.3f} ms", file=sys.stderr, flush=True)
+        print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.4f} ms; sustained {r['sustained']}",
+              file=sys.stderr, flush=True)
     all_configs = None
     if args.all_configs:
         from workloads import WORKLOADS
@@ -331,16 +485,20 @@ def main():
         for name in WORKLOADS:
             r = done.get(name)
             if r is None:
-                r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path)
+                r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups)
             w = r["workload"]
             peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
             all_configs[name] = {
                 "B": w.B, "H": w.H, "N": w.N, "dtype": w.dtype,
                 "value": round(r["value"], 2),
                 "forward_ms": round(r["forward_ms"], 4),
+                "forward_ms_median": round(r["forward_ms_median"], 4),
+                "forward_ms_min": round(r["forward_ms_min"], 4),
                 "forward_tflops": round(r["forward_tflops"], 2),
                 "frac": round(r["forward_tflops"] / peak, 4),
                 "prologue_gbs": round(r["prologue_gbs"], 1),
+                "prologue_gbs_mall_flushed": round(r["prologue_gbs_mall_flushed"], 1),
+                "split_workspace_bytes": r["split_workspace_bytes"],
             }
             print(f"bench: {name} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
     if args.calibrate_copy:
@@ -348,10 +506,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.workload, args.cpu_heads)
+        cpu = cpu_baseline(args.workload, args.cpu_heads, main_res["forward_ms"] * 1e-3)
 
     w = main_res["workload"]
-    traffic = measured_traffic(args.path)
     line = {
         "metric": "joint-attention TFLOP/s and % MFMA peak at N=4608 and N=16896, 1 GPU",
         "value": round(main_res["value"], 2),
@@ -369,28 +526,20 @@ def main():
             "workload": f"{w.name}: 2048x2048 text-to-image with CFG, B={w.B} H={w.H} "
                         f"N={w.n_txt}+{w.grid[0]}x{w.grid[1]}={w.N} d=128, prologue + attention",
             "path": args.path,
-            "groups": args.groups,
+            "split": {"groups": args.groups, "workspace_bytes": main_res["split_workspace_bytes"]},
             "B": w.B, "H": w.H, "N": w.N, "head_dim": 128,
         },
-        "roofline": {
-            "kernel": "attn_fwd_kernel (bf16, %s)" % ("fused query prologue" if args.path == "fused" else "plain"),
-            "bound": "mfma",
-            "achieved": round(main_res["forward_tflops"], 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(main_res["forward_tflops"] / BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "launch_ms": round(main_res["forward_ms"], 4),
-            "counters": measured_mfma_busy("bf16") if args.path == "fused" else None,
-        },
+        "roofline": roofline(main_res, "bf16", args, BF16_PEAK_TFLOPS, "attn_fwd_kernel (bf16, %s)" % (
+            "fused query prologue" if args.path == "fused" else "plain")),
         "prologue": {
             "kernel": "prologue_bf16_kernel (%s)" % ("keys only" if args.path == "fused" else "queries and keys"),
             "bound": "hbm",
             "achieved": round(main_res["prologue_gbs"], 1),
+            "achieved_mall_flushed": round(main_res["prologue_gbs_mall_flushed"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(main_res["prologue_gbs"] / HBM_PEAK_GBS, 4),
-            "launch_us": round(main_res["prologue_us"], 2),
+            "launch_us_median": round(main_res["prologue_us_median"], 2),
         },
         "also": also,
         "fp8": fp8,

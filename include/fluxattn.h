@@ -30,24 +30,31 @@
  *              [N, 3] = (t, h, w) per token, shared by all B and H.  Scales
  *              are fp32 [B, H], contiguous.
  *   Pointers   all data pointers are DEVICE pointers on the current HIP device.
- *              The caller owns every buffer.  The library keeps no per-call
- *              state, allocates nothing and never synchronises; work is
- *              enqueued on `stream` (a hipStream_t; NULL = null stream) and
- *              the call returns at once.
+ *              The caller owns every buffer, including the optional split
+ *              workspace of the _ex attention forms.  The library keeps no
+ *              per-call or process-wide setting, allocates nothing, frees
+ *              nothing and never synchronises; work is enqueued on `stream`
+ *              (a hipStream_t; NULL = null stream) and the call returns at
+ *              once, so every call may be captured into a HIP graph.
  *   Shapes     D == 128; B, H, N >= 1; N <= FLUXATTN_MAX_N; axes even and
  *              summing to D; theta > 0; eps >= 0.
  *   Alignment  q/k/v/o and prologue outputs 16 bytes; pos_ids, weights and
  *              scales 4 bytes.
  *   Errors     validation order: null pointers, shape, alignment, aliasing,
- *              device (must be gfx950).  Any failure returns before anything
+ *              device (must be gfx950), then the split workspace (its plan
+ *              depends on the device).  Any failure returns before anything
  *              is enqueued and leaves every output untouched.  A failed
  *              launch returns FLUXATTN_ERR_HIP (fluxattn_last_hip_error()
  *              gives the hipError_t).  Faults inside a kernel surface at the
  *              caller's next synchronisation, as with any HIP work.
  *   Numerics   inputs are not checked for NaN/Inf; a NaN spreads to the rows
- *              it touches.  No atomics are used: results are bitwise
- *              reproducible run to run.
- *   Threads    every entry point is re-entrant and thread-safe.
+ *              it touches.  Results are bitwise reproducible run to run.
+ *              Launches without a split use no atomics; a split launch
+ *              counts the pieces of each cut query block with one
+ *              device-scope atomic counter and merges them in a fixed
+ *              order, whichever piece arrives last (fluxattn_split).
+ *   Threads    every entry point is re-entrant and thread-safe; calls that
+ *              share a split workspace must not run at the same time.
  */
 #ifndef FLUXATTN_H
 #define FLUXATTN_H
@@ -94,6 +101,47 @@ typedef struct {
     int32_t start[4];
 } fluxattn_streams;
 
+/*
+ * Key-range split of one attention launch (an execution choice: the function
+ * computed is the one each entry point describes).  A launch normally runs
+ * one workgroup per 256-query block of each (b,h), in rounds of one
+ * workgroup per compute unit, and its last round can leave compute units
+ * idle.  A split launch instead runs G persistent workgroups: all but the
+ * last one or two rounds of blocks go whole, in launch order, and the
+ * remaining blocks' (query block, 64-key tile) pairs, in (b, h, query
+ * block, key tile) order, are dealt out as G equal contiguous shares.  A
+ * block whose keys fall in several shares is computed in pieces; each piece
+ * leaves its fp32 partial O, row shift and normaliser in the workspace, and
+ * the piece that arrives last merges them in share order and stores O.
+ * Results differ from the uncut launch by the P roundings (each piece's P
+ * is relative to its own running shift) and fp32 summation order, and are
+ * deterministic.
+ *   groups     0: G = the device's compute units; the launch is cut only
+ *                 with at least two rounds of blocks, when whole blocks
+ *                 would leave more than 3% of the last round idle;
+ *              > 0 (at most 16384): G = groups, at most one per key tile of
+ *                 the cut blocks; always cut (with more workgroups than
+ *                 blocks, blocks are cut into several pieces);
+ *              < 0: never cut (the same as passing no fluxattn_split).
+ *   workspace  device memory of the caller, 256-byte aligned, at least
+ *              fluxattn_split_workspace_bytes() long for the launch, apart
+ *              from every other buffer of the call, and all zero before
+ *              its first use (for example one hipMemset after allocation).
+ *              A launch leaves the arrival counts at its start zero again,
+ *              so a workspace serves any number of launches, with any
+ *              groups, as long as they do not overlap in time (one stream,
+ *              or ordered by events).  NULL is fine for a launch that is
+ *              not cut (fluxattn_split_workspace_bytes() == 0).
+ *   workspace_bytes  its size.
+ * A missing, short, misaligned or overlapping workspace for a launch that
+ * is cut returns FLUXATTN_ERR_WORKSPACE.
+ */
+typedef struct {
+    int32_t groups;
+    void *workspace;
+    uint64_t workspace_bytes;
+} fluxattn_split;
+
 typedef enum {
     FLUXATTN_OK = 0,
     FLUXATTN_ERR_NULL_POINTER = 1,  /* a required pointer is NULL            */
@@ -101,7 +149,9 @@ typedef enum {
     FLUXATTN_ERR_MISALIGNED = 3,    /* a pointer breaks the alignment rule   */
     FLUXATTN_ERR_ALIASING = 4,      /* an output overlaps a buffer it may not */
     FLUXATTN_ERR_NO_DEVICE = 5,     /* no HIP device, or it is not gfx950    */
-    FLUXATTN_ERR_HIP = 6            /* a HIP call (launch) failed            */
+    FLUXATTN_ERR_HIP = 6,           /* a HIP call (launch) failed            */
+    FLUXATTN_ERR_WORKSPACE = 7      /* split workspace missing, too small,
+                                       misaligned or overlapping a buffer  */
 } fluxattn_status;
 
 /*
@@ -257,8 +307,8 @@ fluxattn_status fluxattn_joint_attention_bf16(
  * fp8 form of fluxattn_joint_attention_bf16: E4M3 q, k, v with fp32 [B,H]
  * scales.  The fp8 key prologue writes k_work (E4M3) and k_scale_work
  * (fp32 [B,H], must not overlap k_scale); the queries are dequantised,
- * normalised and rotated in the attention kernel and kept in bf16, which is
- * more precise than the E4M3 Q' of the two-call path.  Output bf16.
+ * normalised and rotated in the attention kernel and re-encoded in E4M3 per
+ * query, as in fluxattn_forward_fused_fp8.  Output bf16.
  */
 fluxattn_status fluxattn_joint_attention_fp8(
     const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -273,11 +323,13 @@ fluxattn_status fluxattn_joint_attention_fp8(
  * Strided, multi-stream forms.  Each takes a fluxattn_layout after every
  * [B,H,N,D] tensor (rules above) and, where norm weights appear, a
  * fluxattn_streams with q_norm_w / k_norm_w as fp32 [streams.count, D]
- * (one row per stream).  Everything else, including aliasing (in place
+ * (one row per stream).  The attention forms (forward, forward_fused,
+ * joint_attention) also take an optional key-range split (fluxattn_split
+ * above; NULL = uncut).  Everything else, including aliasing (in place
  * means the same pointer and the same layout), is as in the contiguous
  * entry point of the same name, which equals its _ex form with contiguous
- * layouts and one stream.  Invalid layouts or streams give
- * FLUXATTN_ERR_INVALID_SHAPE.  For the fp8 prologue, q_scale_out /
+ * layouts, one stream and no split.  Invalid layouts, streams or split
+ * groups give FLUXATTN_ERR_INVALID_SHAPE.  For the fp8 prologue, q_scale_out /
  * k_scale_out are sqrt(D) * max|w| / 448 with the maximum over all
  * streams' rows.  k_work of the joint forms is contiguous [B,H,N,D] and
  * may equal k only when k is contiguous too.
@@ -305,14 +357,37 @@ fluxattn_status fluxattn_forward_ex_bf16(
     const void *q, fluxattn_layout q_layout, const void *k,
     fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
     void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
-    int64_t D, float softmax_scale, void *stream);
+    int64_t D, float softmax_scale, const fluxattn_split *split, void *stream);
 
 fluxattn_status fluxattn_forward_ex_fp8(
     const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
     fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
     const float *q_scale, const float *k_scale, const float *v_scale,
     void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
-    int64_t D, float softmax_scale, void *stream);
+    int64_t D, float softmax_scale, const fluxattn_split *split, void *stream);
+
+/*
+ * Attention on raw queries (fluxattn_forward_fused_bf16 / _fp8) over
+ * strided views, with per-stream query norm weights and an optional split.
+ */
+fluxattn_status fluxattn_forward_fused_ex_bf16(
+    const void *q, fluxattn_layout q_layout, const void *k,
+    fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+    void *o, fluxattn_layout o_layout, const float *q_norm_w,
+    fluxattn_streams streams, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, const fluxattn_split *split, void *stream);
+
+fluxattn_status fluxattn_forward_fused_ex_fp8(
+    const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+    fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+    const float *q_scale, const float *k_scale, const float *v_scale,
+    void *o, fluxattn_layout o_layout, const float *q_norm_w,
+    fluxattn_streams streams, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, const fluxattn_split *split, void *stream);
 
 fluxattn_status fluxattn_joint_attention_ex_bf16(
     const void *q, fluxattn_layout q_layout, const void *k,
@@ -321,7 +396,7 @@ fluxattn_status fluxattn_joint_attention_ex_bf16(
     const float *k_norm_w, fluxattn_streams streams, const int32_t *pos_ids,
     int64_t B, int64_t H, int64_t N, int64_t D,
     int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
-    float softmax_scale, void *stream);
+    float softmax_scale, const fluxattn_split *split, void *stream);
 
 fluxattn_status fluxattn_joint_attention_ex_fp8(
     const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
@@ -331,60 +406,25 @@ fluxattn_status fluxattn_joint_attention_ex_fp8(
     const float *q_norm_w, const float *k_norm_w, fluxattn_streams streams,
     const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
     int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
-    float softmax_scale, void *stream);
+    float softmax_scale, const fluxattn_split *split, void *stream);
+
+/*
+ * Bytes of split workspace (fluxattn_split above) that an attention launch
+ * over B*H heads of N tokens needs with this groups setting: 0 when the
+ * launch would not be cut.  Host-only: enqueues nothing.  groups == 0
+ * depends on the current device's compute units and returns
+ * FLUXATTN_ERR_NO_DEVICE without a gfx950 device.  A launch with
+ * groups > 0 needs 128 KiB plus about 264 KiB per workgroup.
+ */
+fluxattn_status fluxattn_split_workspace_bytes(
+    int64_t B, int64_t H, int64_t N, int64_t D, int32_t groups,
+    uint64_t *bytes);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *fluxattn_status_string(fluxattn_status s);
 
 /* hipError_t of this thread's most recent FLUXATTN_ERR_HIP (0 if none). */
 int fluxattn_last_hip_error(void);
-
-/*
- * Execution setting of every attention launch (forward, fused and joint
- * entry points); the function computed is the one described above.  A
- * launch normally runs one workgroup per 256-query block of each (b,h).
- * A cut launch instead runs G persistent workgroups: all but the last one
- * or two rounds of blocks go whole, in launch order, and the remaining
- * blocks' (query block, 64-key tile) pairs, in (b, h, query block, key
- * tile) order, are dealt out as G equal contiguous shares, so that the
- * last round no longer leaves compute units idle.  A block whose keys fall
- * in several shares is computed in pieces; each piece leaves its fp32
- * partial O, row shift and normaliser in a workspace, and the piece
- * finishing last merges them in share order and stores O.  Results then
- * differ from the uncut launch by the P roundings (each piece's P is
- * relative to its own running shift) and fp32 summation order, and are
- * deterministic.
- *   groups == 0  (default) G = the device's compute units; cut only with
- *                at least two rounds of blocks, when whole blocks would
- *                leave more than 3% of the last round idle.
- *   groups > 0   G = groups, at most one per key tile of the cut blocks;
- *                always cut (with more workgroups than blocks, blocks are
- *                cut into several pieces).
- *   groups < 0   never cut.
- * Process-wide, for launches made after the call.  A cut launch uses a
- * workspace per (device, stream), allocated with hipMalloc by the first
- * such launch on that stream (128 KiB plus about 264 KiB per workgroup)
- * and held until the process ends; launches on one stream share it in
- * stream order, and a launch needing more workgroups than it holds
- * synchronises the stream once to replace it.
- * Returns FLUXATTN_ERR_INVALID_SHAPE for groups > 16384 (setting unchanged).
- */
-fluxattn_status fluxattn_set_forward_groups(int32_t groups);
-
-/* The current setting of fluxattn_set_forward_groups. */
-int32_t fluxattn_get_forward_groups(void);
-
-/*
- * Frees every split workspace the library holds (see
- * fluxattn_set_forward_groups), on every device, after waiting for each
- * such device to finish its work (hipDeviceSynchronize: a workspace's
- * stream may no longer exist).  The next cut launch on a stream allocates
- * again.  Must not run concurrently with attention launches.  With no
- * workspace held it touches no device and returns FLUXATTN_OK; on a HIP
- * error it keeps the workspaces it could not free and returns
- * FLUXATTN_ERR_HIP.
- */
-fluxattn_status fluxattn_release_workspaces(void);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int fluxattn_version(void);

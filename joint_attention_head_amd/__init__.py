@@ -17,10 +17,14 @@ Entry points (same names as the C ABI):
     fluxattn_joint_attention_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, ...)
     fluxattn_joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids, ...)
 and the strided, multi-stream forms fluxattn_qk_norm_rope_ex_{bf16,fp8},
-fluxattn_forward_ex_{bf16,fp8} and fluxattn_joint_attention_ex_{bf16,fp8},
-which accept any [B,H,N,D] tensor view whose last dimension is contiguous
-(for example q, k, v sliced out of a packed [B,N,3,H,D] projection output)
-and per-stream norm weights [S, D] with the streams' first tokens.
+fluxattn_forward_ex_{bf16,fp8}, fluxattn_forward_fused_ex_{bf16,fp8} and
+fluxattn_joint_attention_ex_{bf16,fp8}, which accept any [B,H,N,D] tensor
+view whose last dimension is contiguous (for example q, k, v sliced out of a
+packed [B,N,3,H,D] projection output) and per-stream norm weights [S, D]
+with the streams' first tokens.  The attention _ex forms take an optional
+key-range split (split=SplitWorkspace(...), see split_workspace()), whose
+device workspace the binding allocates with torch, zeroed, like an output;
+the library itself never allocates.
 """
 from __future__ import annotations
 
@@ -44,6 +48,7 @@ STATUS = {
     4: "FLUXATTN_ERR_ALIASING",
     5: "FLUXATTN_ERR_NO_DEVICE",
     6: "FLUXATTN_ERR_HIP",
+    7: "FLUXATTN_ERR_WORKSPACE",
 }
 
 EXPORTS = (
@@ -61,11 +66,11 @@ EXPORTS = (
     "fluxattn_forward_ex_fp8",
     "fluxattn_joint_attention_ex_bf16",
     "fluxattn_joint_attention_ex_fp8",
+    "fluxattn_forward_fused_ex_bf16",
+    "fluxattn_forward_fused_ex_fp8",
+    "fluxattn_split_workspace_bytes",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
-    "fluxattn_set_forward_groups",
-    "fluxattn_get_forward_groups",
-    "fluxattn_release_workspaces",
     "fluxattn_version",
 )
 
@@ -96,8 +101,14 @@ class Streams(ctypes.Structure):
     _fields_ = [("count", ctypes.c_int32), ("start", ctypes.c_int32 * 4)]
 
 
+class Split(ctypes.Structure):
+    """fluxattn_split: key-range split setting and the caller's workspace."""
+    _fields_ = [("groups", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
+
+
 _L = Layout
 _S = Streams
+_SP = ctypes.POINTER(Split)
 
 _SIGS = {
     "fluxattn_qk_norm_rope_bf16": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64,
@@ -118,15 +129,17 @@ _SIGS = {
                                       _i32, _i32, _i32, _f, _f, _p],
     "fluxattn_qk_norm_rope_ex_fp8": [_p, _L, _p, _L, _p, _p, _p, _L, _p, _L, _p, _p, _p, _p, _S, _p, _i64, _i64,
                                      _i64, _i64, _i32, _i32, _i32, _f, _f, _p],
-    "fluxattn_forward_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _i64, _i64, _i64, _i64, _f, _p],
-    "fluxattn_forward_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _L, _i64, _i64, _i64, _i64, _f, _p],
+    "fluxattn_forward_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _i64, _i64, _i64, _i64, _f, _SP, _p],
+    "fluxattn_forward_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _L, _i64, _i64, _i64, _i64, _f, _SP, _p],
+    "fluxattn_forward_fused_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _p, _S, _p, _i64, _i64, _i64, _i64,
+                                       _i32, _i32, _i32, _f, _f, _f, _SP, _p],
+    "fluxattn_forward_fused_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _L, _p, _S, _p, _i64, _i64, _i64,
+                                      _i64, _i32, _i32, _i32, _f, _f, _f, _SP, _p],
     "fluxattn_joint_attention_ex_bf16": [_p, _L, _p, _L, _p, _L, _p, _p, _L, _p, _p, _S, _p, _i64, _i64, _i64,
-                                         _i64, _i32, _i32, _i32, _f, _f, _f, _p],
+                                         _i64, _i32, _i32, _i32, _f, _f, _f, _SP, _p],
     "fluxattn_joint_attention_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _p, _p, _L, _p, _p, _S, _p,
-                                        _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _p],
-    "fluxattn_set_forward_groups": [_i32],
-    "fluxattn_get_forward_groups": [],
-    "fluxattn_release_workspaces": [],
+                                        _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _SP, _p],
+    "fluxattn_split_workspace_bytes": [_i64, _i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_uint64)],
 }
 
 
@@ -320,8 +333,8 @@ def fluxattn_joint_attention_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k
                                  theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, stream=None):
     """The whole block on raw float8_e4m3fn q, k, v with fp32 [B,H] scales:
     the fp8 key prologue into (k_work, k_scale_work), then attention that
-    normalises and rotates the queries as it loads them (kept in bf16).
-    Returns bf16 o."""
+    normalises and rotates the queries as it loads them and re-encodes them
+    in E4M3 per query.  Returns bf16 o."""
     B, H, N, D = _bhnd(q)
     e4 = torch.float8_e4m3fn
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -388,20 +401,52 @@ def fluxattn_forward_fused_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos
 # ---- strided views and token streams
 
 
-def fluxattn_set_forward_groups(groups: int):
-    """Workgroup count G of the attention launches: 0 = one per compute unit
-    with key-range splits only where they balance the last round, > 0 = G
-    (split whenever query blocks outnumber G), < 0 = never split."""
-    _check(lib().fluxattn_set_forward_groups(int(groups)))
+def fluxattn_split_workspace_bytes(B: int, H: int, N: int, groups: int = 0, D: int = HEAD_DIM) -> int:
+    """Bytes of split workspace an attention launch over B*H heads of N
+    tokens needs with this groups setting (0 when it would not be cut)."""
+    n = ctypes.c_uint64(0)
+    _check(lib().fluxattn_split_workspace_bytes(int(B), int(H), int(N), int(D), int(groups), ctypes.byref(n)))
+    return int(n.value)
 
 
-def fluxattn_get_forward_groups() -> int:
-    return int(lib().fluxattn_get_forward_groups())
+class SplitWorkspace:
+    """A key-range split setting with its device workspace: `nbytes` zeroed
+    bytes (torch memory of the binding, not of the library), reusable by any
+    number of launches that do not overlap in time.  groups: 0 = one
+    workgroup per compute unit, cut only where that balances the last round;
+    > 0 = that many workgroups, always cut; < 0 = never cut."""
+
+    def __init__(self, groups: int = 0, nbytes: int = 0, device=None):
+        self.groups = int(groups)
+        self.nbytes = int(nbytes)
+        self.buffer = None
+        if self.nbytes > 0:
+            dev = torch.device("cuda") if device is None else torch.device(device)
+            self.buffer = torch.zeros(self.nbytes, dtype=torch.uint8, device=dev)
+
+    def as_struct(self) -> Split:
+        ptr = None if self.buffer is None else self.buffer.data_ptr()
+        return Split(self.groups, ptr, self.nbytes)
+
+    def counts(self) -> torch.Tensor:
+        """The arrival counts at the start of the workspace (int32), which
+        every launch leaves at zero."""
+        n = min(self.nbytes, 2 * 16384 * 4) // 4
+        return self.buffer[:4 * n].view(torch.int32)
 
 
-def fluxattn_release_workspaces():
-    """Free the split workspaces (after synchronising their devices)."""
-    _check(lib().fluxattn_release_workspaces())
+def split_workspace(B: int, H: int, N: int, groups: int = 0, device=None) -> SplitWorkspace:
+    """A SplitWorkspace sized for attention over B*H heads of N tokens."""
+    return SplitWorkspace(groups, fluxattn_split_workspace_bytes(B, H, N, groups), device)
+
+
+def _split_arg(split):
+    """ctypes argument of an optional split (None: the uncut launch)."""
+    if split is None:
+        return None
+    if not isinstance(split, SplitWorkspace):
+        raise TypeError("split must be a SplitWorkspace or None")
+    return ctypes.byref(split.as_struct())
 
 
 def layout_of(t: torch.Tensor) -> Layout:
@@ -511,9 +556,9 @@ def fluxattn_qk_norm_rope_ex_fp8(q, k, q_scale, k_scale, q_norm_w, k_norm_w, pos
     return q_out, k_out, q_scale_out, k_scale_out
 
 
-def fluxattn_forward_ex_bf16(q, k, v, o=None, softmax_scale=0.0, stream=None):
+def fluxattn_forward_ex_bf16(q, k, v, o=None, softmax_scale=0.0, split=None, stream=None):
     """Attention on bf16 [B,H,N,D] views; o defaults to a new contiguous
-    tensor.  Returns o."""
+    tensor; split: optional SplitWorkspace.  Returns o."""
     shape = tuple(q.shape)
     B, H, N, D = _bhnd(q)
     lq = _need_view(q, "q", torch.bfloat16, shape)
@@ -522,11 +567,13 @@ def fluxattn_forward_ex_bf16(q, k, v, o=None, softmax_scale=0.0, stream=None):
     o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
     lo = _need_view(o, "o", torch.bfloat16, shape)
     _check(lib().fluxattn_forward_ex_bf16(q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, o.data_ptr(),
-                                          lo, B, H, N, D, float(softmax_scale), _stream(stream)))
+                                          lo, B, H, N, D, float(softmax_scale), _split_arg(split),
+                                          _stream(stream)))
     return o
 
 
-def fluxattn_forward_ex_fp8(q, k, v, q_scale, k_scale, v_scale, o=None, softmax_scale=0.0, stream=None):
+def fluxattn_forward_ex_fp8(q, k, v, q_scale, k_scale, v_scale, o=None, softmax_scale=0.0, split=None,
+                            stream=None):
     """fp8 form of fluxattn_forward_ex_bf16 (fp32 [B,H] scales); bf16 o."""
     shape = tuple(q.shape)
     B, H, N, D = _bhnd(q)
@@ -540,13 +587,13 @@ def fluxattn_forward_ex_fp8(q, k, v, q_scale, k_scale, v_scale, o=None, softmax_
     lo = _need_view(o, "o", torch.bfloat16, shape)
     _check(lib().fluxattn_forward_ex_fp8(q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(),
                                          k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lo, B, H, N, D,
-                                         float(softmax_scale), _stream(stream)))
+                                         float(softmax_scale), _split_arg(split), _stream(stream)))
     return o
 
 
 def fluxattn_joint_attention_ex_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, streams=(0,), o=None,
                                      k_work=None, axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS,
-                                     softmax_scale=0.0, stream=None):
+                                     softmax_scale=0.0, split=None, stream=None):
     """The whole block on raw bf16 [B,H,N,D] views with per-stream norm
     weights [S, D].  k_work (contiguous [B,H,N,D]) receives K'; o defaults
     to a new contiguous tensor.  Returns o."""
@@ -566,13 +613,13 @@ def fluxattn_joint_attention_ex_bf16(q, k, v, q_norm_w, k_norm_w, pos_ids, strea
     _check(lib().fluxattn_joint_attention_ex_bf16(
         q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, k_work.data_ptr(), o.data_ptr(), lo,
         q_norm_w.data_ptr(), k_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1],
-        axes[2], float(theta), float(eps), float(softmax_scale), _stream(stream)))
+        axes[2], float(theta), float(eps), float(softmax_scale), _split_arg(split), _stream(stream)))
     return o
 
 
 def fluxattn_joint_attention_ex_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, k_norm_w, pos_ids,
                                     streams=(0,), o=None, k_work=None, k_scale_work=None, axes=ROPE_AXES,
-                                    theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, stream=None):
+                                    theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, split=None, stream=None):
     """fp8 form of fluxattn_joint_attention_ex_bf16; returns bf16 o."""
     shape = tuple(q.shape)
     B, H, N, D = _bhnd(q)
@@ -596,5 +643,52 @@ def fluxattn_joint_attention_ex_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w
         q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(), k_scale.data_ptr(),
         v_scale.data_ptr(), k_work.data_ptr(), k_scale_work.data_ptr(), o.data_ptr(), lo, q_norm_w.data_ptr(),
         k_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta),
-        float(eps), float(softmax_scale), _stream(stream)))
+        float(eps), float(softmax_scale), _split_arg(split), _stream(stream)))
+    return o
+
+
+def fluxattn_forward_fused_ex_bf16(q, k, v, q_norm_w, pos_ids, streams=(0,), o=None, axes=ROPE_AXES,
+                                   theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, split=None, stream=None):
+    """Attention on raw bf16 query views (RMSNorm + RoPE applied as they are
+    loaded, per-stream weights [S, D]) against prepared key views k and
+    value views v; split: optional SplitWorkspace.  Returns o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    st = streams_of(streams)
+    lq = _need_view(q, "q", torch.bfloat16, shape)
+    lk = _need_view(k, "k", torch.bfloat16, shape)
+    lv = _need_view(v, "v", torch.bfloat16, shape)
+    q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    _check(lib().fluxattn_forward_fused_ex_bf16(
+        q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, o.data_ptr(), lo, q_norm_w.data_ptr(), st,
+        pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps),
+        float(softmax_scale), _split_arg(split), _stream(stream)))
+    return o
+
+
+def fluxattn_forward_fused_ex_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, pos_ids, streams=(0,), o=None,
+                                  axes=ROPE_AXES, theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, split=None,
+                                  stream=None):
+    """fp8 form of fluxattn_forward_fused_ex_bf16 (E4M3 views, fp32 [B,H]
+    scales); returns bf16 o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    e4 = torch.float8_e4m3fn
+    st = streams_of(streams)
+    lq = _need_view(q, "q", e4, shape)
+    lk = _need_view(k, "k", e4, shape)
+    lv = _need_view(v, "v", e4, shape)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, (B, H))
+    q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    o = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    _check(lib().fluxattn_forward_fused_ex_fp8(
+        q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), o.data_ptr(), lo, q_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0],
+        axes[1], axes[2], float(theta), float(eps), float(softmax_scale), _split_arg(split), _stream(stream)))
     return o

@@ -6,9 +6,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "fluxattn.h"
 #include "fluxattn_internal.h"
@@ -157,10 +154,6 @@ bool disjoint(const View &a, const View &b, int64_t B, int64_t H, int64_t N, int
 
 // ---- key-range split of the forward launches
 
-// 0: one workgroup per compute unit, split where that balances the work
-// (plan_split); > 0: that many workgroups (at most one per tail key tile),
-// always split; < 0: never.
-std::atomic<int32_t> g_forward_groups{0};
 constexpr int32_t kMaxGroups = 1 << 14;
 
 int32_t compute_units(int dev) {
@@ -178,91 +171,49 @@ int32_t compute_units(int dev) {
   return n;
 }
 
-// Split workspace of one (device, stream): arrival counts (zeroed once at
-// allocation; every launch leaves them at zero) then the partial results.
-// Launches on one stream run in order, so they share it safely; each other
-// stream gets its own.  Held until the process ends.
-struct Workspace {
-  void *p = nullptr;
-  size_t bytes = 0;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
-// One arrival count per tail block (fewer than 2 * groups of them).  The
-// count region has the size for the largest setting whatever the launch's
-// groups, so that the slots after it never move: launches with different
-// group counts share a workspace, and a slot written by one must not land
-// on counts another expects at zero.
-constexpr size_t kSplitCountBytes = static_cast<size_t>(2) * kMaxGroups * sizeof(int32_t);
-size_t split_bytes(int32_t groups) {
-  return kSplitCountBytes + static_cast<size_t>(groups) * 2 * kSplitPieceFloats * sizeof(float);
-}
-
-hipError_t workspace_for(int dev, hipStream_t s, size_t bytes, void **out) {
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace &w = g_ws[std::make_pair(dev, s)];
-  if (w.bytes < bytes) {
-    if (w.p) {
-      hipError_t e = hipStreamSynchronize(s);   // earlier launches on s may still use it
-      if (e != hipSuccess) return e;
-      e = hipFree(w.p);
-      w.p = nullptr;
-      w.bytes = 0;
-      if (e != hipSuccess) return e;
-    }
-    void *p = nullptr;
-    hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    e = hipMemset(p, 0, bytes);
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      return e;
-    }
-    w.p = p;
-    w.bytes = bytes;
-  }
-  *out = w.p;
-  return hipSuccess;
-}
-
-// Fill a.split_* for a forward launch over nb query blocks of key_tiles
-// key tiles each (split_groups stays 0 when the launch is not split).
-hipError_t plan_split(ForwardArgs &a, int64_t nb, int64_t key_tiles, hipStream_t s) {
-  a.split_groups = 0;
-  const int32_t setting = g_forward_groups.load(std::memory_order_relaxed);
-  if (setting < 0 || nb < 1) return hipSuccess;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  int64_t groups = setting > 0 ? setting : compute_units(dev);
+// Persistent workgroups of a launch over nb query blocks of key_tiles key
+// tiles each, or 0 when it runs uncut.  setting: the caller's groups (0:
+// `cus` workgroups, cut only with at least two rounds of blocks and more
+// than 3% of the last round idle; > 0: that many, always cut; < 0: never).
+int64_t split_groups_for(int64_t nb, int64_t key_tiles, int32_t setting, int32_t cus) {
+  if (setting < 0 || nb < 1) return 0;
+  int64_t groups = setting > 0 ? setting : cus;
+  if (groups < 2) return 0;
   if (setting == 0) {
-    if (nb >= 2 * groups) {
-      // whole rounds, then a tail: split when whole blocks would leave
-      // more than 3% of the last round idle
-      const int64_t rounds = (nb + groups - 1) / groups;
-      if (nb * 100 >= rounds * groups * 97) return hipSuccess;
-    } else {
-      // fewer than two rounds: measured slower cut than whole (at one to two
-      // rounds the shares stream keys out of step; with fewer blocks than
-      // compute units the per-job start-up and the merges outweigh the idle
-      // units: N = 1536 runs 19% (bf16) and 26% (fp8) slower cut)
-      return hipSuccess;
-    }
+    // fewer than two rounds: measured slower cut than whole (at one to two
+    // rounds the shares stream keys out of step; with fewer blocks than
+    // compute units the per-job start-up and the merges outweigh the idle
+    // units: N = 1536 runs 19% (bf16) and 26% (fp8) slower cut)
+    if (nb < 2 * groups) return 0;
+    // whole rounds, then a tail: cut when whole blocks would leave more
+    // than 3% of the last round idle
+    const int64_t rounds = (nb + groups - 1) / groups;
+    if (nb * 100 >= rounds * groups * 97) return 0;
   }
-  // every share holds at least one pair of the tail (the merge reads a
-  // slot of every share between a block's first and last)
+  // every share holds at least one pair of the tail (the merge reads a slot
+  // of every share between a block's first and last)
   const int64_t tail = nb >= 2 * groups ? nb - (nb / groups - 1) * groups : nb;
   groups = std::min<int64_t>(groups, tail * key_tiles);
-  if (groups < 2 || (setting == 0 && nb == groups)) return hipSuccess;
-  void *p = nullptr;
-  e = workspace_for(dev, s, split_bytes(static_cast<int32_t>(groups)), &p);
-  if (e != hipSuccess) return e;
-  a.split_cnt = static_cast<int32_t *>(p);
-  a.split_part = reinterpret_cast<float *>(static_cast<char *>(p) + kSplitCountBytes);
-  a.split_groups = static_cast<int32_t>(groups);
-  return hipSuccess;
+  if (groups < 2 || (setting == 0 && nb == groups)) return 0;
+  return groups;
 }
+
+// Split workspace layout: one arrival count per tail block (fewer than
+// 2 * groups of them), then two partial slots per workgroup.  The count
+// region has the size for the largest setting whatever the launch's groups,
+// so that the slots never move: launches with different group counts may
+// share a workspace, and a slot written by one must not land on counts
+// another expects at zero.
+constexpr uint64_t kSplitCountBytes = static_cast<uint64_t>(2) * kMaxGroups * sizeof(int32_t);
+constexpr uint64_t kSplitAlign = 256;
+uint64_t split_bytes(int64_t groups) {
+  return groups > 0 ? kSplitCountBytes + static_cast<uint64_t>(groups) * 2 * kSplitPieceFloats * sizeof(float) : 0;
+}
+
+// The split setting of a call: NULL means never cut.
+int32_t split_setting(const fluxattn_split *sp) { return sp ? sp->groups : -1; }
+
+bool split_setting_ok(const fluxattn_split *sp) { return !sp || sp->groups <= kMaxGroups; }
 
 // gfx950 check, cached per device (arch never changes for a device id).
 fluxattn_status device_ok() {
@@ -403,17 +354,22 @@ fluxattn_status prologue_core(View q, View k, const float *q_scale, const float 
 
 // ---- attention (fused: q is raw and gets RMSNorm + RoPE on load)
 
+// Validation, the split plan and the kernel arguments of one attention
+// launch; nothing is enqueued.  `others` are further buffers of the calling
+// entry point that the split workspace must not overlap.
 template <bool FP8>
-fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const float *k_scale,
-                             const float *v_scale, View o, int64_t B, int64_t H, int64_t N, int64_t D,
-                             float softmax_scale, bool fused, const float *q_norm_w,
-                             const fluxattn_streams &streams, const int32_t *pos_ids, int32_t at, int32_t ah,
-                             int32_t aw, float theta, float eps, void *stream) {
+fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, const float *k_scale,
+                                const float *v_scale, View o, int64_t B, int64_t H, int64_t N, int64_t D,
+                                float softmax_scale, bool fused, const float *q_norm_w,
+                                const fluxattn_streams &streams, const int32_t *pos_ids, int32_t at, int32_t ah,
+                                int32_t aw, float theta, float eps, const fluxattn_split *split,
+                                const Range *others, int n_others, ForwardArgs &a, bool &strided) {
   constexpr int E = FP8 ? 1 : 2;
   if (!q.p || !k.p || !v.p || !o.p) return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!q_scale || !k_scale || !v_scale)) return FLUXATTN_ERR_NULL_POINTER;
   if (fused && (!q_norm_w || !pos_ids)) return FLUXATTN_ERR_NULL_POINTER;
-  if (!shape_ok(B, H, N, D) || !scale_ok(softmax_scale)) return FLUXATTN_ERR_INVALID_SHAPE;
+  if (!shape_ok(B, H, N, D) || !scale_ok(softmax_scale) || !split_setting_ok(split))
+    return FLUXATTN_ERR_INVALID_SHAPE;
   if (fused && (!rope_ok(at, ah, aw, theta, eps) || !streams_ok(streams, N))) return FLUXATTN_ERR_INVALID_SHAPE;
   for (const View *w : {&q, &k, &v})
     if (!strides_ok(*w, D, E) || !head_fits(*w, N, D, E)) return FLUXATTN_ERR_INVALID_SHAPE;
@@ -426,16 +382,41 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
   const Range ro = extent(o, B, H, N, D, 2);
   for (const View *w : {&q, &k, &v})
     if (overlap(ro, extent(*w, B, H, N, D, E))) return FLUXATTN_ERR_ALIASING;
-  {
-    const Plain plains[] = {{q_scale, BH * 4}, {k_scale, BH * 4}, {v_scale, BH * 4},
-                            {fused ? q_norm_w : nullptr, streams.count * D * 4}, {fused ? pos_ids : nullptr, N * 12}};
-    if (!apart(o, B, H, N, D, 2, plains, 5)) return FLUXATTN_ERR_ALIASING;
-  }
+  const Plain plains[] = {{q_scale, BH * 4}, {k_scale, BH * 4}, {v_scale, BH * 4},
+                          {fused ? q_norm_w : nullptr, streams.count * D * 4}, {fused ? pos_ids : nullptr, N * 12}};
+  if (!apart(o, B, H, N, D, 2, plains, 5)) return FLUXATTN_ERR_ALIASING;
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
 
+  // the split plan depends on the device's compute units, so the workspace
+  // is checked after the device
+  const int32_t setting = split_setting(split);
+  int32_t cus = 0;
+  if (setting == 0) {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLUXATTN_ERR_NO_DEVICE;
+    }
+    cus = compute_units(d);
+  }
+  const int64_t groups = split_groups_for(forward_grid_blocks(BH, N), forward_key_tiles(N), setting, cus);
+  if (groups > 0) {
+    const uint64_t need = split_bytes(groups);
+    if (!split->workspace || split->workspace_bytes < need || !aligned(split->workspace, kSplitAlign))
+      return FLUXATTN_ERR_WORKSPACE;
+    const Range ws = span(split->workspace, static_cast<int64_t>(need));
+    for (const View *w : {&q, &k, &v})
+      if (overlap(ws, extent(*w, B, H, N, D, E))) return FLUXATTN_ERR_WORKSPACE;
+    if (overlap(ws, ro)) return FLUXATTN_ERR_WORKSPACE;
+    for (const Plain &pl : plains)
+      if (overlap(ws, span(pl.p, pl.bytes))) return FLUXATTN_ERR_WORKSPACE;
+    for (int i = 0; i < n_others; ++i)
+      if (overlap(ws, others[i])) return FLUXATTN_ERR_WORKSPACE;
+  }
+
   const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / sqrt(static_cast<double>(D));
-  ForwardArgs a{};
+  a = ForwardArgs{};
   a.q = q.p;
   a.k = k.p;
   a.v = v.p;
@@ -468,13 +449,36 @@ fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const
                       : 0.f;
       }
   }
-  const bool strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
-                         is_contiguous(o, H, N, D));
-  const hipError_t ps = plan_split(a, forward_grid_blocks(BH, N), forward_key_tiles(N), static_cast<hipStream_t>(stream));
-  if (ps != hipSuccess) return hip_fail(ps);
+  if (groups > 0) {
+    a.split_cnt = static_cast<int32_t *>(split->workspace);
+    a.split_part = reinterpret_cast<float *>(static_cast<char *>(split->workspace) + kSplitCountBytes);
+    a.split_groups = static_cast<int32_t>(groups);
+  }
+  strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
+              is_contiguous(o, H, N, D));
+  return FLUXATTN_OK;
+}
+
+template <bool FP8>
+fluxattn_status forward_launch(const ForwardArgs &a, bool fused, bool strided, void *stream) {
   const hipError_t e = FP8 ? launch_forward_fp8(a, fused, strided, static_cast<hipStream_t>(stream))
                            : launch_forward_bf16(a, fused, strided, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLUXATTN_OK : hip_fail(e);
+}
+
+template <bool FP8>
+fluxattn_status forward_core(View q, View k, View v, const float *q_scale, const float *k_scale,
+                             const float *v_scale, View o, int64_t B, int64_t H, int64_t N, int64_t D,
+                             float softmax_scale, bool fused, const float *q_norm_w,
+                             const fluxattn_streams &streams, const int32_t *pos_ids, int32_t at, int32_t ah,
+                             int32_t aw, float theta, float eps, const fluxattn_split *split, void *stream) {
+  ForwardArgs a;
+  bool strided = false;
+  const fluxattn_status s =
+      forward_prepare<FP8>(q, k, v, q_scale, k_scale, v_scale, o, B, H, N, D, softmax_scale, fused, q_norm_w, streams,
+                           pos_ids, at, ah, aw, theta, eps, split, nullptr, 0, a, strided);
+  if (s != FLUXATTN_OK) return s;
+  return forward_launch<FP8>(a, fused, strided, stream);
 }
 
 // ---- the whole block: keys-only prologue into k_work (contiguous), then
@@ -485,13 +489,14 @@ fluxattn_status joint_core(View q, View k, View v, const float *q_scale, const f
                            const float *v_scale, void *k_work, float *k_scale_work, View o,
                            const float *q_norm_w, const float *k_norm_w, const fluxattn_streams &streams,
                            const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D, int32_t at,
-                           int32_t ah, int32_t aw, float theta, float eps, float softmax_scale, void *stream) {
+                           int32_t ah, int32_t aw, float theta, float eps, float softmax_scale,
+                           const fluxattn_split *split, void *stream) {
   constexpr int E = FP8 ? 1 : 2;
   if (!q.p || !k.p || !v.p || !k_work || !o.p || !q_norm_w || !k_norm_w || !pos_ids)
     return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!q_scale || !k_scale || !v_scale || !k_scale_work)) return FLUXATTN_ERR_NULL_POINTER;
   if (!shape_ok(B, H, N, D) || !rope_ok(at, ah, aw, theta, eps) || !scale_ok(softmax_scale) ||
-      !streams_ok(streams, N))
+      !streams_ok(streams, N) || !split_setting_ok(split))
     return FLUXATTN_ERR_INVALID_SHAPE;
   View kw = contiguous(k_work, H, N, D);
   for (const View *w : {&q, &k, &v})
@@ -528,12 +533,21 @@ fluxattn_status joint_core(View q, View k, View v, const float *q_scale, const f
   }
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
-  // both calls re-validate a subset of the above and cannot fail it
-  fluxattn_status s = prologue_core<FP8>(View{}, k, nullptr, k_scale, View{}, kw, nullptr, k_scale_work, nullptr,
-                                         k_norm_w, streams, pos_ids, B, H, N, D, at, ah, aw, theta, eps, stream);
+  // the attention launch (and its split workspace, which must not overlap
+  // the raw keys and their weights either) is checked before the prologue
+  // is enqueued; both calls re-validate a subset of the above and cannot
+  // fail it
+  const Range others[] = {extent(k, B, H, N, D, E), span(k_norm_w, S * D * 4)};
+  ForwardArgs fa;
+  bool strided = false;
+  fluxattn_status s =
+      forward_prepare<FP8>(q, kw, v, q_scale, k_scale_work, v_scale, o, B, H, N, D, softmax_scale, true, q_norm_w,
+                           streams, pos_ids, at, ah, aw, theta, eps, split, others, 2, fa, strided);
   if (s != FLUXATTN_OK) return s;
-  return forward_core<FP8>(q, kw, v, q_scale, k_scale_work, v_scale, o, B, H, N, D, softmax_scale, true, q_norm_w,
-                           streams, pos_ids, at, ah, aw, theta, eps, stream);
+  s = prologue_core<FP8>(View{}, k, nullptr, k_scale, View{}, kw, nullptr, k_scale_work, nullptr, k_norm_w, streams,
+                         pos_ids, B, H, N, D, at, ah, aw, theta, eps, stream);
+  if (s != FLUXATTN_OK) return s;
+  return forward_launch<FP8>(fa, true, strided, stream);
 }
 
 const fluxattn_streams kOneStream = {1, {0, 0, 0, 0}};
@@ -594,7 +608,7 @@ fluxattn_status fluxattn_forward_bf16(const void *q, const void *k, const void *
                                       int64_t H, int64_t N, int64_t D, float softmax_scale, void *stream) {
   return forward_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr,
                              nullptr, nullptr, contiguous(o, H, N, D), B, H, N, D, softmax_scale, false, nullptr,
-                             kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, stream);
+                             kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, nullptr, stream);
 }
 
 fluxattn_status fluxattn_forward_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -603,26 +617,27 @@ fluxattn_status fluxattn_forward_fp8(const uint8_t *q, const uint8_t *k, const u
                                      float softmax_scale, void *stream) {
   return forward_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale,
                             k_scale, v_scale, contiguous(o, H, N, D), B, H, N, D, softmax_scale, false, nullptr,
-                            kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, stream);
+                            kOneStream, nullptr, 0, 0, 0, 0.f, 0.f, nullptr, stream);
 }
 
 fluxattn_status fluxattn_forward_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
                                          fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
                                          void *o, fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N,
-                                         int64_t D, float softmax_scale, void *stream) {
+                                         int64_t D, float softmax_scale, const fluxattn_split *split,
+                                         void *stream) {
   return forward_core<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
                              nullptr, view_of(o, o_layout), B, H, N, D, softmax_scale, false, nullptr, kOneStream,
-                             nullptr, 0, 0, 0, 0.f, 0.f, stream);
+                             nullptr, 0, 0, 0, 0.f, 0.f, split, stream);
 }
 
 fluxattn_status fluxattn_forward_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
                                         fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
                                         const float *q_scale, const float *k_scale, const float *v_scale, void *o,
                                         fluxattn_layout o_layout, int64_t B, int64_t H, int64_t N, int64_t D,
-                                        float softmax_scale, void *stream) {
+                                        float softmax_scale, const fluxattn_split *split, void *stream) {
   return forward_core<true>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), q_scale, k_scale,
                             v_scale, view_of(o, o_layout), B, H, N, D, softmax_scale, false, nullptr, kOneStream,
-                            nullptr, 0, 0, 0, 0.f, 0.f, stream);
+                            nullptr, 0, 0, 0, 0.f, 0.f, split, stream);
 }
 
 fluxattn_status fluxattn_forward_fused_bf16(const void *q, const void *k, const void *v, void *o,
@@ -632,7 +647,7 @@ fluxattn_status fluxattn_forward_fused_bf16(const void *q, const void *k, const 
                                             void *stream) {
   return forward_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr,
                              nullptr, nullptr, contiguous(o, H, N, D), B, H, N, D, softmax_scale, true, q_norm_w,
-                             kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, stream);
+                             kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, nullptr, stream);
 }
 
 fluxattn_status fluxattn_forward_fused_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -643,7 +658,7 @@ fluxattn_status fluxattn_forward_fused_fp8(const uint8_t *q, const uint8_t *k, c
                                            void *stream) {
   return forward_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale,
                             k_scale, v_scale, contiguous(o, H, N, D), B, H, N, D, softmax_scale, true, q_norm_w,
-                            kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, stream);
+                            kOneStream, pos_ids, axes_t, axes_h, axes_w, theta, eps, nullptr, stream);
 }
 
 fluxattn_status fluxattn_joint_attention_bf16(const void *q, const void *k, const void *v, void *k_work,
@@ -653,7 +668,7 @@ fluxattn_status fluxattn_joint_attention_bf16(const void *q, const void *k, cons
                                               float theta, float eps, float softmax_scale, void *stream) {
   return joint_core<false>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), nullptr, nullptr,
                            nullptr, k_work, nullptr, contiguous(o, H, N, D), q_norm_w, k_norm_w, kOneStream, pos_ids,
-                           B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+                           B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, nullptr, stream);
 }
 
 fluxattn_status fluxattn_joint_attention_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v,
@@ -665,7 +680,7 @@ fluxattn_status fluxattn_joint_attention_fp8(const uint8_t *q, const uint8_t *k,
                                              float theta, float eps, float softmax_scale, void *stream) {
   return joint_core<true>(contiguous(q, H, N, D), contiguous(k, H, N, D), contiguous(v, H, N, D), q_scale, k_scale,
                           v_scale, k_work, k_scale_work, contiguous(o, H, N, D), q_norm_w, k_norm_w, kOneStream,
-                          pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+                          pos_ids, B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, nullptr, stream);
 }
 
 fluxattn_status fluxattn_joint_attention_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
@@ -675,10 +690,10 @@ fluxattn_status fluxattn_joint_attention_ex_bf16(const void *q, fluxattn_layout 
                                                  fluxattn_streams streams, const int32_t *pos_ids, int64_t B,
                                                  int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
                                                  int32_t axes_w, float theta, float eps, float softmax_scale,
-                                                 void *stream) {
+                                                 const fluxattn_split *split, void *stream) {
   return joint_core<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
                            nullptr, k_work, nullptr, view_of(o, o_layout), q_norm_w, k_norm_w, streams, pos_ids, B, H,
-                           N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+                           N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, split, stream);
 }
 
 fluxattn_status fluxattn_joint_attention_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
@@ -689,10 +704,55 @@ fluxattn_status fluxattn_joint_attention_ex_fp8(const uint8_t *q, fluxattn_layou
                                                 const float *k_norm_w, fluxattn_streams streams,
                                                 const int32_t *pos_ids, int64_t B, int64_t H, int64_t N, int64_t D,
                                                 int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta,
-                                                float eps, float softmax_scale, void *stream) {
+                                                float eps, float softmax_scale, const fluxattn_split *split,
+                                                void *stream) {
   return joint_core<true>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), q_scale, k_scale,
                           v_scale, k_work, k_scale_work, view_of(o, o_layout), q_norm_w, k_norm_w, streams, pos_ids,
-                          B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, stream);
+                          B, H, N, D, axes_t, axes_h, axes_w, theta, eps, softmax_scale, split, stream);
+}
+
+fluxattn_status fluxattn_forward_fused_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                               fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+                                               void *o, fluxattn_layout o_layout, const float *q_norm_w,
+                                               fluxattn_streams streams, const int32_t *pos_ids, int64_t B,
+                                               int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
+                                               int32_t axes_w, float theta, float eps, float softmax_scale,
+                                               const fluxattn_split *split, void *stream) {
+  return forward_core<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
+                             nullptr, view_of(o, o_layout), B, H, N, D, softmax_scale, true, q_norm_w, streams,
+                             pos_ids, axes_t, axes_h, axes_w, theta, eps, split, stream);
+}
+
+fluxattn_status fluxattn_forward_fused_ex_fp8(const uint8_t *q, fluxattn_layout q_layout, const uint8_t *k,
+                                              fluxattn_layout k_layout, const uint8_t *v, fluxattn_layout v_layout,
+                                              const float *q_scale, const float *k_scale, const float *v_scale,
+                                              void *o, fluxattn_layout o_layout, const float *q_norm_w,
+                                              fluxattn_streams streams, const int32_t *pos_ids, int64_t B, int64_t H,
+                                              int64_t N, int64_t D, int32_t axes_t, int32_t axes_h, int32_t axes_w,
+                                              float theta, float eps, float softmax_scale,
+                                              const fluxattn_split *split, void *stream) {
+  return forward_core<true>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), q_scale, k_scale,
+                            v_scale, view_of(o, o_layout), B, H, N, D, softmax_scale, true, q_norm_w, streams, pos_ids,
+                            axes_t, axes_h, axes_w, theta, eps, split, stream);
+}
+
+fluxattn_status fluxattn_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t groups,
+                                               uint64_t *bytes) {
+  if (!bytes) return FLUXATTN_ERR_NULL_POINTER;
+  if (!shape_ok(B, H, N, D) || groups > kMaxGroups) return FLUXATTN_ERR_INVALID_SHAPE;
+  int32_t cus = 0;
+  if (groups == 0) {
+    const fluxattn_status dev = device_ok();
+    if (dev != FLUXATTN_OK) return dev;
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) {
+      (void)hipGetLastError();
+      return FLUXATTN_ERR_NO_DEVICE;
+    }
+    cus = compute_units(d);
+  }
+  *bytes = split_bytes(split_groups_for(forward_grid_blocks(B * H, N), forward_key_tiles(N), groups, cus));
+  return FLUXATTN_OK;
 }
 
 const char *fluxattn_status_string(fluxattn_status s) {
@@ -704,42 +764,13 @@ const char *fluxattn_status_string(fluxattn_status s) {
     case FLUXATTN_ERR_ALIASING: return "output overlaps another buffer";
     case FLUXATTN_ERR_NO_DEVICE: return "no gfx950 HIP device";
     case FLUXATTN_ERR_HIP: return "HIP runtime error";
+    case FLUXATTN_ERR_WORKSPACE: return "split workspace missing, too small, misaligned or overlapping";
   }
   return "unknown status";
 }
 
 int fluxattn_last_hip_error(void) { return g_last_hip_error; }
 
-fluxattn_status fluxattn_set_forward_groups(int32_t groups) {
-  if (groups > kMaxGroups) return FLUXATTN_ERR_INVALID_SHAPE;
-  g_forward_groups.store(groups, std::memory_order_relaxed);
-  return FLUXATTN_OK;
-}
-
-int32_t fluxattn_get_forward_groups(void) { return g_forward_groups.load(std::memory_order_relaxed); }
-
-fluxattn_status fluxattn_release_workspaces(void) {
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  if (g_ws.empty()) return FLUXATTN_OK;
-  int prev = 0;
-  hipError_t first = hipGetDevice(&prev);
-  if (first != hipSuccess) return hip_fail(first);
-  for (auto it = g_ws.begin(); it != g_ws.end();) {
-    hipError_t e = hipSetDevice(it->first.first);
-    if (e == hipSuccess) e = hipDeviceSynchronize();   // its stream may be gone: wait for the device
-    if (e == hipSuccess && it->second.p) e = hipFree(it->second.p);
-    if (e != hipSuccess) {
-      if (first == hipSuccess) first = e;
-      ++it;   // keep what could not be freed
-      continue;
-    }
-    it = g_ws.erase(it);
-  }
-  const hipError_t r = hipSetDevice(prev);
-  if (first == hipSuccess) first = r;
-  return first == hipSuccess ? FLUXATTN_OK : hip_fail(first);
-}
-
-int fluxattn_version(void) { return 130; }
+int fluxattn_version(void) { return 20000; }
 
 }  // extern "C"

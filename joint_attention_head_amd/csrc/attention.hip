@@ -165,7 +165,6 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
-  const int rank = gw * 64 + lane;             // 0..255 inside the group
   // wave-uniform job fields (they address the scalar buffer descriptors)
   const int bh = __builtin_amdgcn_readfirstlane(job.bh), qt = __builtin_amdgcn_readfirstlane(job.qt);
   const int kt0 = __builtin_amdgcn_readfirstlane(job.kt0), T = __builtin_amdgcn_readfirstlane(job.T);

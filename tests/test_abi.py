@@ -11,7 +11,7 @@ import joint_attention_head_amd as fa
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fluxattn.h")
 
-OK, NULLP, SHAPE, ALIGN, ALIAS, NODEV, HIPERR = range(7)
+OK, NULLP, SHAPE, ALIGN, ALIAS, NODEV, HIPERR, WORKSPACE = range(8)
 
 
 def declared_functions():
@@ -36,8 +36,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(7):
-        assert lib.fluxattn_status_string(s).decode()
+    for s in range(8):
+        assert lib.fluxattn_status_string(s).decode() != "unknown status"
     assert lib.fluxattn_status_string(99) == b"unknown status"
     assert lib.fluxattn_version() >= 100
     assert lib.fluxattn_last_hip_error() == 0
@@ -95,27 +95,54 @@ def fused8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, o=O, wq=WQ, pos=POS, b=B, h=
                                           0.0, None)
 
 
-def test_forward_groups_setting(lib):
-    """Host-only setting: round-trips, rejects counts above 16384 and keeps
-    the previous value then."""
-    assert lib.fluxattn_get_forward_groups() == 0          # default
-    try:
-        for g in (-1, 3, 256, 16384, 0):
-            assert lib.fluxattn_set_forward_groups(g) == OK
-            assert lib.fluxattn_get_forward_groups() == g
-        assert lib.fluxattn_set_forward_groups(5) == OK
-        assert lib.fluxattn_set_forward_groups(16385) == SHAPE
-        assert lib.fluxattn_get_forward_groups() == 5
-    finally:
-        lib.fluxattn_set_forward_groups(0)
+# Split workspace layout: 2 * 16384 int32 arrival counts, then two partial
+# slots per workgroup of 512 threads x (64 fp32 accumulators + shift and
+# normaliser).
+COUNT_BYTES = 2 * 16384 * 4
+SLOT_BYTES = 512 * (64 + 2) * 4
 
 
-def test_release_workspaces_without_any_is_a_no_op(lib):
-    """Without a GPU no split launch can have run: nothing to free, so it
-    returns OK without touching a device (with workspaces held it would
-    free them)."""
-    assert lib.fluxattn_release_workspaces() == OK
-    assert lib.fluxattn_last_hip_error() == 0
+def ws_bytes(lib, b, h, n, groups, d=D):
+    out = ctypes.c_uint64(12345)
+    st = lib.fluxattn_split_workspace_bytes(b, h, n, d, groups, ctypes.byref(out))
+    return st, out.value
+
+
+def test_split_workspace_bytes_is_host_only(lib):
+    """The workspace a split launch needs, computed without a device for an
+    explicit workgroup count: N = 1000 gives 4 query blocks of 256 per head
+    and 16 key tiles, so B*H = 2 heads are 8 blocks."""
+    assert ws_bytes(lib, 1, 2, 1000, 3) == (OK, COUNT_BYTES + 3 * 2 * SLOT_BYTES)
+    assert ws_bytes(lib, 1, 2, 1000, 7) == (OK, COUNT_BYTES + 7 * 2 * SLOT_BYTES)
+    # more workgroups than blocks: at most one per key tile of the 8 blocks
+    assert ws_bytes(lib, 1, 2, 1000, 100) == (OK, COUNT_BYTES + 100 * 2 * SLOT_BYTES)
+    assert ws_bytes(lib, 1, 2, 1000, 200) == (OK, COUNT_BYTES + 128 * 2 * SLOT_BYTES)
+    assert ws_bytes(lib, 1, 2, 1000, 1) == (OK, 0)        # one workgroup: never cut
+    assert ws_bytes(lib, 1, 2, 1000, -1) == (OK, 0)
+    assert ws_bytes(lib, 1, 2, 1000, 16384)[0] == OK
+    assert ws_bytes(lib, 1, 2, 1000, 16385)[0] == SHAPE
+    assert ws_bytes(lib, 1, 2, 1000, 3, d=64)[0] == SHAPE
+    assert lib.fluxattn_split_workspace_bytes(1, 2, 1000, D, 3, None) == NULLP
+    # the default setting depends on the device's compute units
+    assert ws_bytes(lib, 2, 24, 16896, 0)[0] == NODEV
+
+
+def test_library_imports_no_allocation_or_synchronisation():
+    """Every entry point enqueues work and returns: the library does not
+    even import an allocation, free, memset or synchronisation call of the
+    HIP runtime (the split workspace comes from the caller)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("binutils nm is not installed")
+    out = subprocess.run([nm, "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    hip = sorted(n for n in imported if n.lower().startswith("hip"))
+    assert hip, "no HIP imports found: wrong file?"
+    banned = re.compile(r"(Malloc|Free|Memset|Memcpy|Synchronize|StreamCreate|Alloc|HostRegister)", re.I)
+    assert [n for n in hip if banned.search(n)] == [], hip
 
 
 def test_null_pointers(lib):

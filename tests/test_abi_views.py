@@ -2,12 +2,14 @@
 stream validation, the aliasing rules for views that share a packed QKV
 tensor, and the binding's layout helpers.  Calls use fake device addresses
 and never get past validation (a valid call stops at the device check)."""
+import ctypes
+
 import pytest
 import torch
 
 import joint_attention_head_amd as fa
 
-OK, NULLP, SHAPE, ALIGN, ALIAS, NODEV, HIPERR = range(7)
+OK, NULLP, SHAPE, ALIGN, ALIAS, NODEV, HIPERR, WORKSPACE = range(8)
 
 B, H, N, D = 2, 3, 320, 128
 WQ, WK, POS = 0x90000000, 0x90001000, 0x90002000
@@ -64,28 +66,48 @@ def prologue8(lib, q=Q, lq=None, k=K, lk=None, qo=QO, lqo=None, ko=KO, lko=None,
                                             B, H, N, D, 16, 56, 56, 1e4, 1e-6, None)
 
 
-def forward(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, n=N):
+def split_arg(split):
+    return None if split is None else ctypes.byref(split)
+
+
+def forward(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, n=N, split=None):
     lq, lk, lv, lo = (x or contig(n=n) for x in (lq, lk, lv, lo))
-    return lib.fluxattn_forward_ex_bf16(q, lq, k, lk, v, lv, o, lo, B, H, n, D, 0.0, None)
+    return lib.fluxattn_forward_ex_bf16(q, lq, k, lk, v, lv, o, lo, B, H, n, D, 0.0, split_arg(split), None)
 
 
-def forward8(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None):
+def forward8(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, split=None):
     lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
-    return lib.fluxattn_forward_ex_fp8(q, lq, k, lk, v, lv, SQ, SK, SV, o, lo, B, H, N, D, 0.0, None)
+    return lib.fluxattn_forward_ex_fp8(q, lq, k, lk, v, lv, SQ, SK, SV, o, lo, B, H, N, D, 0.0, split_arg(split),
+                                       None)
 
 
-def joint(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, kw=KW, o=O, lo=None, wq=WQ, wk=WK, st=None):
+def fused(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, wq=WQ, st=None, split=None):
+    lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
+    st = st or streams(0)
+    return lib.fluxattn_forward_fused_ex_bf16(q, lq, k, lk, v, lv, o, lo, wq, st, POS, B, H, N, D, 16, 56, 56, 1e4,
+                                              1e-6, 0.0, split_arg(split), None)
+
+
+def fused8(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, st=None, split=None):
+    lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
+    st = st or streams(0)
+    return lib.fluxattn_forward_fused_ex_fp8(q, lq, k, lk, v, lv, SQ, SK, SV, o, lo, WQ, st, POS, B, H, N, D, 16,
+                                             56, 56, 1e4, 1e-6, 0.0, split_arg(split), None)
+
+
+def joint(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, kw=KW, o=O, lo=None, wq=WQ, wk=WK, st=None,
+          split=None):
     lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
     st = st or streams(0)
     return lib.fluxattn_joint_attention_ex_bf16(q, lq, k, lk, v, lv, kw, o, lo, wq, wk, st, POS, B, H, N, D,
-                                                16, 56, 56, 1e4, 1e-6, 0.0, None)
+                                                16, 56, 56, 1e4, 1e-6, 0.0, split_arg(split), None)
 
 
-def joint8(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, kw=KW, skw=SKW, o=O, lo=None, st=None):
+def joint8(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, kw=KW, skw=SKW, o=O, lo=None, st=None, split=None):
     lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
     st = st or streams(0)
     return lib.fluxattn_joint_attention_ex_fp8(q, lq, k, lk, v, lv, SQ, SK, SV, kw, skw, o, lo, WQ, WK, st, POS,
-                                               B, H, N, D, 16, 56, 56, 1e4, 1e-6, 0.0, None)
+                                               B, H, N, D, 16, 56, 56, 1e4, 1e-6, 0.0, split_arg(split), None)
 
 
 def test_contiguous_layouts_and_one_stream_are_valid(lib):
@@ -93,8 +115,20 @@ def test_contiguous_layouts_and_one_stream_are_valid(lib):
     assert prologue8(lib) == NODEV
     assert forward(lib) == NODEV
     assert forward8(lib) == NODEV
+    assert fused(lib) == NODEV
+    assert fused8(lib) == NODEV
     assert joint(lib) == NODEV
     assert joint8(lib) == NODEV
+
+
+def test_split_groups_are_validated_before_the_device(lib):
+    """A split setting above 16384 workgroups is an invalid parameter;
+    a valid one (even without a workspace) gets as far as the device check:
+    the workspace is checked after it, against the device's plan."""
+    for g, want in ((16385, SHAPE), (16384, NODEV), (5, NODEV), (0, NODEV), (-1, NODEV)):
+        sp = fa.Split(g, None, 0)
+        for call in (forward, forward8, fused, fused8, joint, joint8):
+            assert call(lib, split=sp) == want, (call.__name__, g)
 
 
 def test_packed_qkv_views_are_valid_and_disjoint(lib):

@@ -255,6 +255,17 @@ def _q_rounded_e4m3(qp, k_scale):
     return codes * 2.0 ** e / g
 
 
+def _no_less_accurate(got, two_call, plain, what):
+    """The fused path's error against the unrounded chain is within 1.5x
+    (plus a rounding step of the output) of the error that the two-call
+    path's one rounding of Q' alone gives, in max-abs and mean-abs."""
+    e, e2 = np.abs(got - plain), np.abs(two_call - plain)
+    _flush(f"{what} vs plain chain: max_abs={e.max():.3e} mean_abs={e.mean():.3e}; "
+           f"two-call rounding alone: max_abs={e2.max():.3e} mean_abs={e2.mean():.3e}")
+    assert e.max() <= 1.5 * e2.max() + 4e-3, what
+    assert e.mean() <= 1.5 * e2.mean() + 2e-4, what
+
+
 @pytest.mark.parametrize("growth", ["rising", "falling", "spike"])
 def test_forward_fused_bf16_logit_range_across_tiles(growth):
     """The running shift of the fused kernel (whose QK^T accumulators start
@@ -268,10 +279,17 @@ def test_forward_fused_bf16_logit_range_across_tiles(growth):
     k = (inp.k.float() * f[None, None, :, None]).to(torch.bfloat16)
     o = fa.fluxattn_forward_fused_bf16(dev(inp.q), dev(k), dev(inp.v), dev(inp.w_q), dev(inp.pos))
     torch.cuda.synchronize()
-    qr = _q_rounded_bf16(_q_prime(f64(inp.q), inp.w_q, inp.pos))
+    qp = _q_prime(f64(inp.q), inp.w_q, inp.pos)
+    qr = _q_rounded_bf16(qp)
     ref = oracle.attention(qr, f64(k), f64(inp.v))
     rel = check_close(f64(o), ref, BF16_TOL, f"fused logit range {growth}")
     assert rel < 1e-2
+    # against the plain chain (no rounding at all): no less accurate than
+    # the two-call path's rounding of Q' itself to bf16 (the prologue's
+    # output), which at these logits is also outside the tolerance
+    plain = oracle.attention(qp, f64(k), f64(inp.v))
+    two_call = oracle.attention(torch.from_numpy(qp).to(torch.bfloat16).double().numpy(), f64(k), f64(inp.v))
+    _no_less_accurate(f64(o), two_call, plain, f"fused logit range {growth}")
 
 
 @pytest.mark.parametrize("fused", [False, True])
@@ -294,7 +312,8 @@ def test_forward_fp8_logit_range_across_tiles(growth, fused):
     args = (dev(inp.q), dev(k8), dev(inp.v), dev(inp.q_scale), dev(sk), dev(inp.v_scale))
     if fused:
         o = fa.fluxattn_forward_fused_fp8(*args, dev(inp.w_q), dev(inp.pos))
-        qr = _q_rounded_e4m3(_q_prime(f64(inp.q, inp.q_scale), inp.w_q, inp.pos), sk)
+        qp = _q_prime(f64(inp.q, inp.q_scale), inp.w_q, inp.pos)
+        qr = _q_rounded_e4m3(qp, sk)
     else:
         o = fa.fluxattn_forward_fp8(*args)
         qr = f64(inp.q, inp.q_scale)
@@ -302,6 +321,15 @@ def test_forward_fp8_logit_range_across_tiles(growth, fused):
     ref = oracle.attention(qr, f64(k8, sk), f64(inp.v, inp.v_scale))
     rel = check_close(f64(o), ref, FP8_TOL, f"fp8 {'fused ' if fused else ''}logit range {growth}")
     assert rel < 1e-1
+    if fused:
+        # against the plain chain: no less accurate than the two-call path,
+        # whose prologue stores Q' in E4M3 with the per-head output scale
+        # sqrt(D) max|w| / 448
+        plain = oracle.attention(qp, f64(k8, sk), f64(inp.v, inp.v_scale))
+        s_out = math.sqrt(128) * float(inp.w_q.abs().max()) / 448.0
+        q2 = torch.from_numpy(qp / s_out).to(torch.float8_e4m3fn).double().numpy() * s_out
+        two_call = oracle.attention(q2, f64(k8, sk), f64(inp.v, inp.v_scale))
+        _no_less_accurate(f64(o), two_call, plain, f"fp8 fused logit range {growth}")
 
 
 def test_forward_bf16_invariants():
@@ -380,7 +408,10 @@ def test_joint_bf16_parity_t2i_2048_sampled():
     got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
     rel = check_close(got, joint_ref(inp, heads, rows), BF16_TOL, "joint bf16 t2i sampled")
     assert rel < 1e-2
-    # V == 1 on the full-size launch
+    # V == 1 on the full-size launch gives exactly 1 in bf16: l sums the
+    # fp32 probabilities and P.V the bf16-rounded ones, so O / l is
+    # sum(bf16(p)) / sum(p), within 2^-9 of 1, which the output rounding
+    # takes to exactly 1 (the ratio itself is not 1 in fp32)
     ones = fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), torch.ones_like(o))
     torch.cuda.synchronize()
     assert torch.all(ones == 1.0)
@@ -455,17 +486,42 @@ def test_keys_only_prologue_and_fused_forward_compose_the_joint_call():
     assert torch.equal(o_parts.view(torch.int16), o_joint.view(torch.int16))
 
 
+def block_rows(N, offsets=(0, 101, 255)):
+    """A few rows of every 256-query block: whatever blocks a launch cuts
+    into key ranges, each of them is sampled."""
+    rows = (np.arange(0, N, 256)[:, None] + np.asarray(offsets)[None, :]).ravel()
+    return np.unique(np.concatenate([rows[rows < N], np.arange(min(32, N)), np.arange(max(0, N - 48), N)]))
+
+
 def test_joint_fused_bf16_t2i_2048_sampled():
-    _flush("joint fused bf16 t2i_2048_cfg (N=16896, B=2, H=24)")
+    """The launches the benchmark times at 2048x2048 text-to-image (B=2,
+    H=24, N=16896): keys-only prologue, then the fused attention with the
+    default key-range split (3168 query blocks on one workgroup per compute
+    unit: 11 whole rounds, then a tail of 352 blocks in equal shares, most
+    of them cut in two).  Checked on rows of every query block of a head of
+    the whole rounds (0,0), of the head where the tail starts (1,18) and of
+    the last head (1,23), against the whole fp64 chain."""
+    _flush("joint fused bf16 t2i_2048_cfg (N=16896, B=2, H=24), benchmark launches")
     inp = inputs("t2i_2048_cfg")
-    o = fa.fluxattn_joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k),
-                                         dev(inp.pos))
+    B, H, N = inp.q.shape[:3]
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    ws = fa.split_workspace(B, H, N, 0)
+    assert ws.nbytes > 0, "the default setting cuts this launch"
+    _, kn = fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos)
+    o = fa.fluxattn_forward_fused_ex_bf16(q, kn, v, w_q, pos, split=ws)
     torch.cuda.synchronize()
-    heads = [(1, 0), (0, 7)]
-    rows = sample_rows(inp.q.shape[2])
+    assert not ws.counts().any()
+    heads = [(0, 0), (1, 18), (1, 23)]
+    rows = block_rows(N)
     got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
-    rel = check_close(got, joint_ref(inp, heads, rows), BF16_TOL, "joint fused bf16 t2i sampled")
+    rel = check_close(got, joint_ref(inp, heads, rows), BF16_TOL, "joint fused bf16 t2i sampled (split)")
     assert rel < 1e-2
+    # the whole-block entry point (uncut) agrees on the same rows
+    o2 = fa.fluxattn_joint_attention_bf16(q, k, v, w_q, w_k, pos)
+    torch.cuda.synchronize()
+    got2 = np.stack([f64(o2[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    check_close(got2, joint_ref(inp, heads, rows), BF16_TOL, "joint fused bf16 t2i sampled (uncut)")
 
 
 def test_joint_fused_fp8_parity():
@@ -508,6 +564,7 @@ def test_joint_fp8_parity_tiny():
 def test_fp8_i2i_2048_sampled():
     _flush("fp8 i2i_2048 (N=33280, H=24)")
     inp = inputs("i2i_2048")
+    B, H, N = inp.q.shape[:3]
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     sq, sk, sv = dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale)
     heads = [(0, 0), (0, 17)]
@@ -527,9 +584,19 @@ def test_fp8_i2i_2048_sampled():
     got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
     rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fp8 i2i sampled")
     assert rel < 1e-1
-    # the whole block with the fused query prologue
-    o = fa.fluxattn_joint_attention_fp8(q, k, v, sq, sk, sv, dev(inp.w_q), dev(inp.w_k), dev(inp.pos))
+    # the launches the benchmark times: keys-only fp8 prologue, then the
+    # fused attention with the default split (3120 query blocks: 11 whole
+    # rounds, then a tail of 304 blocks, heads 21 (from block 86) to 23, in
+    # equal shares); rows of every query block of a head of the whole
+    # rounds and of two tail heads
+    ws = fa.split_workspace(B, H, N, 0)
+    assert ws.nbytes > 0, "the default setting cuts this launch"
+    _, kn, _, skn = fa.fluxattn_qk_norm_rope_fp8(None, k, None, sk, None, dev(inp.w_k), dev(inp.pos))
+    o = fa.fluxattn_forward_fused_ex_fp8(q, kn, v, sq, skn, sv, dev(inp.w_q), dev(inp.pos), split=ws)
     torch.cuda.synchronize()
+    assert not ws.counts().any()
+    heads = [(0, 0), (0, 21), (0, 23)]
+    rows = block_rows(N, offsets=(0, 255))
     got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
-    rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fused fp8 i2i sampled")
+    rel = check_close(got, joint_ref(inp, heads, rows), FP8_TOL, "joint fused fp8 i2i sampled (split)")
     assert rel < 1e-1

@@ -2,20 +2,19 @@
 
 With G persistent workgroups each taking an equal share of the (query
 block, key tile) pairs, a query block can be computed in several key
-ranges whose partial results the last piece to finish merges.  The split
-is forced here at sizes the fp64 oracle handles by setting G below or
-above the number of 256-query blocks; every case spans several 64-key
-tiles, with a ragged last key tile and a ragged last query block.  Checked: parity with the
-oracle (same tolerances as the uncut launch), closeness to the uncut launch
-(a piece that starts inside a block takes its first row shift from its own
-first tile, so its P values are rounded relative to another shift: the two
-launches differ by that rounding and fp32 summation order, far inside the
-oracle tolerance), bitwise determinism (the merge is symmetric in the two
-pieces, so arrival order does not matter), and that a launch leaves the
-arrival counts at zero (a later launch on other inputs is still right).
+ranges whose partial results the last piece to finish merges, in a split
+workspace the caller provides.  The split is forced here at sizes the fp64
+oracle handles by setting G below or above the number of 256-query blocks;
+every case spans several 64-key tiles, with a ragged last key tile and a
+ragged last query block.  Checked: parity with the oracle (same tolerances
+as the uncut launch), closeness to the uncut launch (a piece that starts
+inside a block takes its first row shift from its own first tile, so its P
+values are rounded relative to another shift: the two launches differ by
+that rounding and fp32 summation order, far inside the oracle tolerance),
+bitwise determinism (the merge sums the pieces in share order, so arrival
+order does not matter), that a launch leaves the workspace's arrival counts
+at zero, and that a short workspace is refused before anything runs.
 """
-import contextlib
-
 import numpy as np
 import pytest
 import torch
@@ -42,14 +41,11 @@ def _flush(msg):
     print(msg, flush=True)
 
 
-@contextlib.contextmanager
-def forward_groups(g):
-    old = fa.fluxattn_get_forward_groups()
-    fa.fluxattn_set_forward_groups(g)
-    try:
-        yield
-    finally:
-        fa.fluxattn_set_forward_groups(old)
+def workspace(inp, groups):
+    B, H, N = inp.q.shape[:3]
+    ws = fa.split_workspace(B, H, N, groups)
+    assert groups <= 1 or ws.nbytes > 0, "forced settings always cut"
+    return ws
 
 
 def inputs(shape, dtype="bf16", seed=0):
@@ -90,24 +86,24 @@ def n_blocks(inp):
     return B * H * ((N + 255) // 256)
 
 
-def forward_bf16(inp):
-    return fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), dev(inp.v))
+def forward_bf16(inp, split=None):
+    return fa.fluxattn_forward_ex_bf16(dev(inp.q), dev(inp.k), dev(inp.v), split=split)
 
 
-def joint_bf16(inp):
-    return fa.fluxattn_joint_attention_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k),
-                                            dev(inp.pos))
+def joint_bf16(inp, split=None):
+    return fa.fluxattn_joint_attention_ex_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.w_k),
+                                               dev(inp.pos), split=split)
 
 
-def forward_fp8(inp):
-    return fa.fluxattn_forward_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale),
-                                   dev(inp.v_scale))
+def forward_fp8(inp, split=None):
+    return fa.fluxattn_forward_ex_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale),
+                                      dev(inp.v_scale), split=split)
 
 
-def joint_fp8(inp):
-    return fa.fluxattn_joint_attention_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale),
-                                           dev(inp.k_scale), dev(inp.v_scale), dev(inp.w_q), dev(inp.w_k),
-                                           dev(inp.pos))
+def joint_fp8(inp, split=None):
+    return fa.fluxattn_joint_attention_ex_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale),
+                                              dev(inp.k_scale), dev(inp.v_scale), dev(inp.w_q), dev(inp.w_k),
+                                              dev(inp.pos), split=split)
 
 
 def attention_ref(inp):
@@ -136,24 +132,25 @@ def test_split_matches_oracle_and_uncut_launch(path, shape):
     run, ref_fn, dtype, tol = PATHS[path]
     inp = inputs(shape, dtype)
     ref = ref_fn(inp)
-    with forward_groups(-1):
-        whole = run(inp)
+    whole = run(inp)
     for g in GROUPS:
         _flush(f"split {path} {shape} groups={g}")
-        with forward_groups(g):
-            o = run(inp)
+        ws = workspace(inp, g)
+        o = run(inp, ws)
         torch.cuda.synchronize()
         check_close(f64(o), ref, tol, f"split {path} {shape} G={g}")
         close_to_uncut(o, whole, dtype, f"split {path} {shape} G={g}")
+        assert not ws.counts().any(), "arrival counts left non-zero"
 
 
 def test_split_is_deterministic_and_leaves_counts_at_zero():
     a, b = inputs("n1000", seed=0), inputs("n1000", seed=5)
-    with forward_groups(3):
-        o1 = forward_bf16(a)
-        ob = forward_bf16(b)     # other inputs: stale counts would merge a's partials
-        o2 = forward_bf16(a)
+    ws = workspace(a, 3)
+    o1 = forward_bf16(a, ws)
+    ob = forward_bf16(b, ws)     # other inputs: stale counts would merge a's partials
+    o2 = forward_bf16(a, ws)
     torch.cuda.synchronize()
+    assert not ws.counts().any()
     check_close(f64(ob), attention_ref(b), BF16_TOL, "split second launch, other inputs")
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
@@ -165,52 +162,60 @@ def test_split_strided_layout():
     tm = lambda t: t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
     q, k, v = tm(inp.q), tm(inp.k), tm(inp.v)
     o = torch.empty(B, N, H, D, dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
-    with forward_groups(5):
-        fa.fluxattn_forward_ex_bf16(q, k, v, o=o)
+    fa.fluxattn_forward_ex_bf16(q, k, v, o=o, split=workspace(inp, 5))
     torch.cuda.synchronize()
     check_close(f64(o), attention_ref(inp), BF16_TOL, "split strided n667 G=5")
 
 
-def test_split_default_setting_flux_dev_1024():
-    """FLUX-dev 1024x1024 (B=1, H=24, N=4608: 432 query blocks): the default
-    setting cuts blocks on a device with fewer compute units than blocks;
-    the result is close to the uncut launch and matches the oracle on
-    sampled rows of two heads."""
-    w = custom_workload(1, 24, 512, (64, 64))
+def test_split_default_setting_cuts_three_rounds():
+    """B=1, H=24, N = 512 + 64x80 = 5632: 528 query blocks, just over two
+    rounds of 256 compute units, so the default setting (groups = 0) cuts
+    the tail (one whole round, then 272 blocks shared by all workgroups).
+    The workspace query says so, the result differs bitwise from the uncut
+    launch (so the cut happened), stays close to it, and matches the oracle
+    on rows of every query block of a whole-round head (0), the head where
+    the tail starts (11) and the last head (23)."""
+    w = custom_workload(1, 24, 512, (64, 80))
     inp = make_inputs(w)
-    with forward_groups(0):
-        o = forward_bf16(inp)
-    with forward_groups(-1):
-        whole = forward_bf16(inp)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 24 * ((w.N + 255) // 256)
+    assert blocks >= 2 * cus and blocks % cus, (blocks, cus)   # the default rule cuts this shape
+    ws = fa.split_workspace(1, 24, w.N, 0)
+    assert ws.nbytes > 0
+    o = forward_bf16(inp, ws)
+    whole = forward_bf16(inp)
     torch.cuda.synchronize()
-    close_to_uncut(o, whole, "bf16", "default setting N=4608")
-    rows = np.unique(np.concatenate([np.arange(40), np.arange(4560, 4608), np.arange(0, 4608, 97)]))
-    for h in (0, 23):
+    assert not torch.equal(o.view(torch.int16), whole.view(torch.int16))
+    close_to_uncut(o, whole, "bf16", "default setting N=5632")
+    assert not ws.counts().any()
+    rows = np.unique(np.concatenate([np.arange(0, w.N, 256)[:, None] + np.array([0, 97, 200, 255])]).ravel())
+    rows = rows[rows < w.N]
+    for h in (0, 11, 23):
         sl = (slice(0, 1), slice(h, h + 1))
         ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
-        check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"default setting N=4608 head {h}")
+        check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"default setting N=5632 head {h}")
 
 
 def test_split_on_two_streams_at_once():
-    """Each stream has its own split workspace: cut launches on two streams
-    that run at the same time give bitwise the results of running them one
-    after the other."""
+    """Cut launches on two streams that run at the same time, each with its
+    own workspace, give bitwise the results of running them one after the
+    other."""
     a, b = inputs("n1000", seed=0), inputs("n1000", seed=7)
     qa, ka, va = dev(a.q), dev(a.k), dev(a.v)
     qb, kb, vb = dev(b.q), dev(b.k), dev(b.v)
-    with forward_groups(3):
-        ref_a = fa.fluxattn_forward_bf16(qa, ka, va)
-        ref_b = fa.fluxattn_forward_bf16(qb, kb, vb)
-        torch.cuda.synchronize()
-        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-        outs = []
-        for _ in range(4):
-            with torch.cuda.stream(s1):
-                oa = fa.fluxattn_forward_bf16(qa, ka, va)
-            with torch.cuda.stream(s2):
-                ob = fa.fluxattn_forward_bf16(qb, kb, vb)
-            outs.append((oa, ob))
-        torch.cuda.synchronize()
+    wa, wb = workspace(a, 3), workspace(b, 3)
+    ref_a = fa.fluxattn_forward_ex_bf16(qa, ka, va, split=wa)
+    ref_b = fa.fluxattn_forward_ex_bf16(qb, kb, vb, split=wb)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            oa = fa.fluxattn_forward_ex_bf16(qa, ka, va, split=wa)
+        with torch.cuda.stream(s2):
+            ob = fa.fluxattn_forward_ex_bf16(qb, kb, vb, split=wb)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
     for oa, ob in outs:
         assert torch.equal(oa.view(torch.int16), ref_a.view(torch.int16))
         assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
@@ -224,10 +229,8 @@ def test_split_many_pieces_flux_dev_512():
     launch, and the oracle on sampled rows of two heads.  (The default
     setting leaves this size uncut: measured faster.)"""
     inp = make_inputs(custom_workload(1, 24, 512, (32, 32)))
-    with forward_groups(256):
-        o = forward_bf16(inp)
-    with forward_groups(-1):
-        whole = forward_bf16(inp)
+    o = forward_bf16(inp, workspace(inp, 256))
+    whole = forward_bf16(inp)
     torch.cuda.synchronize()
     close_to_uncut(o, whole, "bf16", "256 workgroups N=1536")
     rows = np.unique(np.concatenate([np.arange(40), np.arange(1500, 1536), np.arange(0, 1536, 37)]))
@@ -238,32 +241,39 @@ def test_split_many_pieces_flux_dev_512():
 
 
 def test_split_workspace_shared_across_group_counts():
-    """Launches with different group counts share one stream's workspace:
-    a small count's partial slots must not land on the arrival counts a
-    larger count expects at zero (G = 100 needs 200 counts, G = 5 ten).
-    G = 100 also cuts each of the 8 blocks into about a dozen pieces."""
+    """Launches with different group counts share one workspace: a small
+    count's partial slots must not land on the arrival counts a larger
+    count expects at zero (G = 100 needs 200 counts, G = 5 ten).  G = 100
+    also cuts each of the 8 blocks into about a dozen pieces."""
     inp = inputs("n1000")
-    with forward_groups(-1):
-        whole = forward_bf16(inp)
+    whole = forward_bf16(inp)
     ref = attention_ref(inp)
+    ws = workspace(inp, 100)
     for g in (100, 5, 100, 5):
-        with forward_groups(g):
-            o = forward_bf16(inp)
+        ws.groups = g
+        o = forward_bf16(inp, ws)
         torch.cuda.synchronize()
         check_close(f64(o), ref, BF16_TOL, f"shared workspace G={g}")
         close_to_uncut(o, whole, "bf16", f"shared workspace G={g}")
 
 
-def test_release_workspaces_then_cut_again():
-    """After the workspaces are freed, the next cut launch allocates a fresh
-    one and is right."""
+def test_short_or_missing_workspace_is_refused_before_launch():
+    """A cut launch without enough workspace returns FLUXATTN_ERR_WORKSPACE
+    and enqueues nothing (the output keeps its contents); a launch that is
+    not cut needs none."""
     inp = inputs("n667")
-    ref = attention_ref(inp)
-    with forward_groups(5):
-        o1 = forward_bf16(inp)
-        torch.cuda.synchronize()
-        fa.fluxattn_release_workspaces()
-        o2 = forward_bf16(inp)
+    B, H, N = inp.q.shape[:3]
+    need = fa.fluxattn_split_workspace_bytes(B, H, N, 5)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    o = torch.full(inp.q.shape, 7.0, dtype=torch.bfloat16, device=DEV)
+    for ws in (fa.SplitWorkspace(5, 0), fa.SplitWorkspace(5, need - 256)):
+        with pytest.raises(fa.FluxAttnError) as e:
+            fa.fluxattn_forward_ex_bf16(q, k, v, o=o, split=ws)
+        assert e.value.status == 7
     torch.cuda.synchronize()
-    check_close(f64(o2), ref, BF16_TOL, "cut after release")
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.all(o == 7.0)
+    # uncut settings run without a workspace
+    for g in (-1, 1):
+        fa.fluxattn_forward_ex_bf16(q, k, v, o=o, split=fa.SplitWorkspace(g, 0))
+    torch.cuda.synchronize()
+    check_close(f64(o), attention_ref(inp), BF16_TOL, "uncut setting, no workspace")

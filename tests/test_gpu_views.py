@@ -224,9 +224,9 @@ def test_joint_ex_bf16_packed_streams_parity(case):
 FP8_CASES = {
     "t2i_77+256_B2": (2, 3, 77, (16, 16), None),
     # three streams at N = 449: E4M3 Q', K' and P alone put the mean error
-    # of a 171-token sequence at about 4.1e-3 (CPU emulation of those
-    # roundings, any seed), the size of the tolerance itself; it falls as
-    # the keys per query grow (2.7e-3 here, 3e-4 at the 33280-token I2I)
+    # at about 2.8e-3 here (tests/test_fp8_rounding_model.py); the
+    # 171-token sequence, where they alone exceed the tolerance, has its own
+    # test below
     "i2i_9+320+120": (1, 2, 9, (16, 20), (10, 12)),
 }
 
@@ -247,6 +247,39 @@ def test_joint_ex_fp8_packed_streams_parity():
         got = np.stack([f64(o[b, h]) for b in range(B) for h in range(H)])
         rel = check_close(got, joint_ref(inp, starts, w_q, w_k, fp8=True), FP8_TOL, f"joint_ex fp8 {case}")
         assert rel < 1e-1
+
+
+def test_joint_ex_fp8_packed_streams_171_tokens_within_the_rounding_model():
+    """The 171-token, three-stream fp8 sequence (9 text + 10x12 target +
+    6x7 reference tokens).  The E4M3 roundings of K', Q' and P alone put its
+    mean-abs error at about 4.3e-3, above the 4e-3 tolerance (the CPU model
+    in tests/fp8_roundings.py, pinned in tests/test_fp8_rounding_model.py),
+    so the kernel is held to that model: mean-abs within 10% of the
+    model's, max-abs and relative L2 within the fp8 tolerance."""
+    import fp8_roundings as fr
+    w = custom_workload(1, 2, 9, (10, 12), (6, 7), "fp8", 12)
+    _flush(f"joint_ex fp8 packed streams N={w.N}")
+    inp = make_inputs(w)
+    starts = stream_starts(w)
+    w_q, w_k = stream_norm_weights(len(starts), seed=w.seed)
+    p, views = packed(inp.q.view(torch.uint8), inp.k.view(torch.uint8), inp.v.view(torch.uint8))
+    qv, kv, vv = (t.view(torch.float8_e4m3fn) for t in views)
+    sc = [dev(s) for s in (inp.q_scale, inp.k_scale, inp.v_scale)]
+    o = fa.fluxattn_joint_attention_ex_fp8(qv, kv, vv, *sc, dev(w_q), dev(w_k), dev(inp.pos), streams=starts)
+    torch.cuda.synchronize()
+    ref = joint_ref(inp, starts, w_q, w_k, fp8=True)
+    q, k, v, wqt, wkt, pos = fr.case_inputs(inp, w_q.double().numpy(), w_k.double().numpy(), starts)
+    model = fr.fused_fp8_model(q, k, v, wqt, wkt, w_k.double().numpy(), pos)[0]
+    m_err = np.abs(model - ref)
+    got = np.stack([f64(o[0, h]) for h in range(inp.q.shape[1])])
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    _flush(f"fp8 N={w.N}: kernel mean_abs={err.mean():.3e} max_abs={err.max():.3e} rel_l2={rel:.3e}; "
+           f"rounding model mean_abs={m_err.mean():.3e} max_abs={m_err.max():.3e}")
+    assert np.isfinite(got).all()
+    assert err.mean() <= 1.1 * m_err.mean()
+    assert err.max() <= FP8_TOL[0]
+    assert rel < 1e-1
 
 
 def test_joint_ex_bf16_t2i_2048_packed_streams_sampled():
