@@ -420,6 +420,36 @@ fluxattn_status fluxattn_split_workspace_bytes(
     int64_t B, int64_t H, int64_t N, int64_t D, int32_t groups,
     uint64_t *bytes);
 
+/*
+ * fluxattn_forward_fused_ex_bf16 with a split of `groups` workgroups
+ * (fluxattn_split.groups) whose workspace is a static array of the library
+ * instead of caller memory: for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid it).
+ *   Limit: a split of at most 256 workgroups (66.1 MiB, one per compute unit
+ *          of an MI355X, the default setting's launch there); a launch
+ *          whose split would need more returns FLUXATTN_ERR_WORKSPACE
+ *          before anything is enqueued.  Launches that are not cut use no
+ *          scratch.
+ *   Memory: each device this entry point runs on holds its own copy of the
+ *          array until the process ends; the first call on a device looks
+ *          it up and clears its arrival counts on `stream`.
+ *   Threads: every call on one device shares that device's array, which
+ *          keeps the last call's partial results; calls that overlap in
+ *          time on one device race (one stream, or order them by events).
+ * Arguments, checks, numerics and errors are those of
+ * fluxattn_forward_fused_ex_bf16 (validation runs before anything is
+ * enqueued); results are bitwise those of that entry point with the same
+ * groups.
+ */
+fluxattn_status fluxattn_forward_fused_noalloc_bf16(
+    const void *q, fluxattn_layout q_layout, const void *k,
+    fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+    void *o, fluxattn_layout o_layout, const float *q_norm_w,
+    fluxattn_streams streams, const int32_t *pos_ids,
+    int64_t B, int64_t H, int64_t N, int64_t D,
+    int32_t axes_t, int32_t axes_h, int32_t axes_w, float theta, float eps,
+    float softmax_scale, int32_t groups, void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *fluxattn_status_string(fluxattn_status s);
 

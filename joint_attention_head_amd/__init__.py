@@ -69,6 +69,7 @@ EXPORTS = (
     "fluxattn_forward_fused_ex_bf16",
     "fluxattn_forward_fused_ex_fp8",
     "fluxattn_split_workspace_bytes",
+    "fluxattn_forward_fused_noalloc_bf16",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
     "fluxattn_version",
@@ -140,6 +141,8 @@ _SIGS = {
     "fluxattn_joint_attention_ex_fp8": [_p, _L, _p, _L, _p, _L, _p, _p, _p, _p, _p, _p, _L, _p, _p, _S, _p,
                                         _i64, _i64, _i64, _i64, _i32, _i32, _i32, _f, _f, _f, _SP, _p],
     "fluxattn_split_workspace_bytes": [_i64, _i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_uint64)],
+    "fluxattn_forward_fused_noalloc_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _p, _S, _p, _i64, _i64, _i64, _i64,
+                                            _i32, _i32, _i32, _f, _f, _f, _i32, _p],
 }
 
 
@@ -691,4 +694,26 @@ def fluxattn_forward_fused_ex_fp8(q, k, v, q_scale, k_scale, v_scale, q_norm_w, 
         q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, q_scale.data_ptr(), k_scale.data_ptr(),
         v_scale.data_ptr(), o.data_ptr(), lo, q_norm_w.data_ptr(), st, pos_ids.data_ptr(), B, H, N, D, axes[0],
         axes[1], axes[2], float(theta), float(eps), float(softmax_scale), _split_arg(split), _stream(stream)))
+    return o
+
+
+def fluxattn_forward_fused_noalloc_bf16(q, k, v, q_norm_w, pos_ids, o, streams=(0,), axes=ROPE_AXES,
+                                        theta=ROPE_THETA, eps=RMS_EPS, softmax_scale=0.0, groups=0, stream=None):
+    """fluxattn_forward_fused_ex_bf16 with a split of `groups` workgroups in
+    the library's static scratch (at most 256 workgroups): for code that must
+    not allocate.  o is required (the binding allocates nothing here either).
+    Returns o."""
+    shape = tuple(q.shape)
+    B, H, N, D = _bhnd(q)
+    st = streams_of(streams)
+    lq = _need_view(q, "q", torch.bfloat16, shape)
+    lk = _need_view(k, "k", torch.bfloat16, shape)
+    lv = _need_view(v, "v", torch.bfloat16, shape)
+    q_norm_w = _weights(q_norm_w, "q_norm_w", st.count, D)
+    _need(pos_ids, "pos_ids", torch.int32, (N, 3))
+    lo = _need_view(o, "o", torch.bfloat16, shape)
+    _check(lib().fluxattn_forward_fused_noalloc_bf16(
+        q.data_ptr(), lq, k.data_ptr(), lk, v.data_ptr(), lv, o.data_ptr(), lo, q_norm_w.data_ptr(), st,
+        pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps),
+        float(softmax_scale), int(groups), _stream(stream)))
     return o

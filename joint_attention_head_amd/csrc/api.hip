@@ -154,8 +154,6 @@ bool disjoint(const View &a, const View &b, int64_t B, int64_t H, int64_t N, int
 
 // ---- key-range split of the forward launches
 
-constexpr int32_t kMaxGroups = 1 << 14;
-
 int32_t compute_units(int dev) {
   static std::atomic<int32_t> cache[64];
   if (dev >= 0 && dev < 64) {
@@ -204,11 +202,7 @@ int64_t split_groups_for(int64_t nb, int64_t key_tiles, int32_t setting, int32_t
 // so that the slots never move: launches with different group counts may
 // share a workspace, and a slot written by one must not land on counts
 // another expects at zero.
-constexpr uint64_t kSplitCountBytes = static_cast<uint64_t>(2) * kMaxGroups * sizeof(int32_t);
-constexpr uint64_t kSplitAlign = 256;
-uint64_t split_bytes(int64_t groups) {
-  return groups > 0 ? kSplitCountBytes + static_cast<uint64_t>(groups) * 2 * kSplitPieceFloats * sizeof(float) : 0;
-}
+uint64_t split_bytes(int64_t groups) { return groups > 0 ? split_workspace_bytes_for(groups) : 0; }
 
 // The split setting of a call: NULL means never cut.
 int32_t split_setting(const fluxattn_split *sp) { return sp ? sp->groups : -1; }
@@ -363,7 +357,8 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
                                 float softmax_scale, bool fused, const float *q_norm_w,
                                 const fluxattn_streams &streams, const int32_t *pos_ids, int32_t at, int32_t ah,
                                 int32_t aw, float theta, float eps, const fluxattn_split *split,
-                                const Range *others, int n_others, ForwardArgs &a, bool &strided) {
+                                const Range *others, int n_others, ForwardArgs &a, bool &strided,
+                                uint64_t *need_out = nullptr) {
   constexpr int E = FP8 ? 1 : 2;
   if (!q.p || !k.p || !v.p || !o.p) return FLUXATTN_ERR_NULL_POINTER;
   if (FP8 && (!q_scale || !k_scale || !v_scale)) return FLUXATTN_ERR_NULL_POINTER;
@@ -401,6 +396,11 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
     cus = compute_units(d);
   }
   const int64_t groups = split_groups_for(forward_grid_blocks(BH, N), forward_key_tiles(N), setting, cus);
+  if (need_out) {
+    // validation only: report the workspace the launch needs
+    *need_out = split_bytes(groups);
+    return FLUXATTN_OK;
+  }
   if (groups > 0) {
     const uint64_t need = split_bytes(groups);
     if (!split->workspace || split->workspace_bytes < need || !aligned(split->workspace, kSplitAlign))
@@ -553,6 +553,28 @@ fluxattn_status joint_core(View q, View k, View v, const float *q_scale, const f
 const fluxattn_streams kOneStream = {1, {0, 0, 0, 0}};
 
 }  // namespace
+
+namespace fluxattn {
+
+fluxattn_status record_hip_error(hipError_t e) { return hip_fail(e); }
+
+fluxattn_status check_forward_fused_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                            fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+                                            void *o, fluxattn_layout o_layout, const float *q_norm_w,
+                                            const fluxattn_streams &streams, const int32_t *pos_ids, int64_t B,
+                                            int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
+                                            int32_t axes_w, float theta, float eps, float softmax_scale,
+                                            int32_t groups, uint64_t *need_bytes) {
+  const fluxattn_split sp = {groups, nullptr, 0};
+  ForwardArgs a;
+  bool strided = false;
+  return forward_prepare<false>(view_of(q, q_layout), view_of(k, k_layout), view_of(v, v_layout), nullptr, nullptr,
+                                nullptr, view_of(o, o_layout), B, H, N, D, softmax_scale, true, q_norm_w, streams,
+                                pos_ids, axes_t, axes_h, axes_w, theta, eps, &sp, nullptr, 0, a, strided,
+                                need_bytes);
+}
+
+}  // namespace fluxattn
 
 extern "C" {
 

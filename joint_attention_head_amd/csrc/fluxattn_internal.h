@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fluxattn.h"
+
 namespace fluxattn {
 
 constexpr int kHeadDim = 128;
@@ -83,6 +85,17 @@ struct ForwardArgs {
 constexpr int kSplitThreads = 512;
 constexpr int64_t kSplitPieceFloats = (int64_t)kSplitThreads * 64 + (int64_t)kSplitThreads * 2;
 
+// Split workspace: one int32 arrival count per tail block, in a region
+// sized for the largest setting (2 * kMaxGroups counts, so that the slots
+// after it never move whatever a launch's groups), then two partial slots
+// per workgroup.  256-byte aligned.
+constexpr int32_t kMaxGroups = 1 << 14;
+constexpr uint64_t kSplitCountBytes = static_cast<uint64_t>(2) * kMaxGroups * sizeof(int32_t);
+constexpr uint64_t kSplitAlign = 256;
+constexpr uint64_t split_workspace_bytes_for(int64_t groups) {
+  return kSplitCountBytes + static_cast<uint64_t>(groups) * 2 * kSplitPieceFloats * sizeof(float);
+}
+
 hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t,
                                 hipStream_t s);
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t,
@@ -98,5 +111,21 @@ hipError_t launch_forward_fp8(const ForwardArgs &a, bool fused, bool strided, hi
 // tokens, and key tiles per head.
 int64_t forward_grid_blocks(int64_t BH, int64_t N);
 int64_t forward_key_tiles(int64_t N);
+
+// Keeps e for fluxattn_last_hip_error() on this thread; returns
+// FLUXATTN_ERR_HIP.
+fluxattn_status record_hip_error(hipError_t e);
+
+// Every check of fluxattn_forward_fused_ex_bf16 with a split of `groups`
+// workgroups except the workspace's, enqueueing nothing; on success
+// *need_bytes is the split workspace the launch needs (0 when it is not
+// cut).
+fluxattn_status check_forward_fused_ex_bf16(const void *q, fluxattn_layout q_layout, const void *k,
+                                            fluxattn_layout k_layout, const void *v, fluxattn_layout v_layout,
+                                            void *o, fluxattn_layout o_layout, const float *q_norm_w,
+                                            const fluxattn_streams &streams, const int32_t *pos_ids, int64_t B,
+                                            int64_t H, int64_t N, int64_t D, int32_t axes_t, int32_t axes_h,
+                                            int32_t axes_w, float theta, float eps, float softmax_scale,
+                                            int32_t groups, uint64_t *need_bytes);
 
 }  // namespace fluxattn

@@ -121,6 +121,26 @@ def test_contiguous_layouts_and_one_stream_are_valid(lib):
     assert joint8(lib) == NODEV
 
 
+def noalloc(lib, q=Q, lq=None, k=K, lk=None, v=V, lv=None, o=O, lo=None, st=None, groups=0):
+    lq, lk, lv, lo = (x or contig() for x in (lq, lk, lv, lo))
+    st = st or streams(0)
+    return lib.fluxattn_forward_fused_noalloc_bf16(q, lq, k, lk, v, lv, o, lo, WQ, st, POS, B, H, N, D, 16, 56, 56,
+                                                   1e4, 1e-6, 0.0, groups, None)
+
+
+def test_noalloc_entry_point_validates_like_the_workspace_form(lib):
+    """The static-scratch form runs every check of the fused _ex form before
+    it looks up its scratch: without a GPU a valid call stops at the device
+    check, and argument errors come first."""
+    assert noalloc(lib) == NODEV
+    assert noalloc(lib, groups=5) == NODEV
+    assert noalloc(lib, groups=16385) == SHAPE
+    assert noalloc(lib, q=None) == NULLP
+    assert noalloc(lib, q=Q + 8) == ALIGN
+    assert noalloc(lib, o=Q) == ALIAS
+    assert noalloc(lib, lo=fa.Layout(0, 0, 64)) == SHAPE
+
+
 def test_split_groups_are_validated_before_the_device(lib):
     """A split setting above 16384 workgroups is an invalid parameter;
     a valid one (even without a workspace) gets as far as the device check:
