@@ -128,7 +128,7 @@ def parse():
     p.add_argument("--no-all-configs", dest="all_configs", action="store_false",
                    help="skip the per-workload table (every workload's forward TFLOP/s and MFMA fraction)")
     p.add_argument("--no-clock", dest="clock", action="store_false",
-                   help="skip the sustained-clock sample (one second of attention launches per kernel)")
+                   help="skip the sustained-clock sample (2.5 s of attention launches per kernel)")
     p.add_argument("--cpu-heads", type=int, default=12, help="(b,h) heads in the CPU oracle sample")
     p.add_argument("--path", choices=("fused", "unfused"), default="fused")
     p.add_argument("--groups", type=int, default=0,
@@ -149,8 +149,9 @@ def stats(xs):
 
 
 class ClockSampler:
-    """Graphics clock and socket power of GPU 0 through amdsmi (None where
-    the library or the query is not available)."""
+    """Graphics clock (mean over the XCDs) and socket power of GPU 0 from the
+    amdsmi metrics table, which the firmware refreshes about once a second
+    (None where the library or the query is not available)."""
 
     def __init__(self):
         self.h = None
@@ -165,22 +166,20 @@ class ClockSampler:
     def read(self):
         if self.h is None:
             return None, None
-        clk = power = None
         try:
-            clk = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.SYS)["clk"]
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
         except Exception:
-            pass
-        try:
-            info = self.amdsmi.amdsmi_get_power_info(self.h)
-            power = info.get("current_socket_power") or info.get("average_socket_power")
-        except Exception:
-            pass
-        return clk, power
+            return None, None
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 65535]
+        clk = sum(clks) / len(clks) if clks else None
+        power = m.get("current_socket_power")
+        return clk, power if isinstance(power, (int, float)) else None
 
-    def during(self, fn, seconds=1.0):
+    def during(self, fn, seconds=2.5):
         """Run fn() back to back for about `seconds` while sampling every
-        10 ms; median clock (MHz) and power (W) of the samples taken after
-        the first quarter (the clock settles under load)."""
+        50 ms; median clock (MHz, mean over XCDs) and power (W) of the
+        samples after the first second (the table lags and the clock
+        settles under load)."""
         import threading
 
         import torch
@@ -191,7 +190,7 @@ class ClockSampler:
         def poll():
             while not stop.is_set():
                 samples.append((time.perf_counter(), *self.read()))
-                time.sleep(0.01)
+                time.sleep(0.05)
 
         th = threading.Thread(target=poll, daemon=True)
         t0 = time.perf_counter()
@@ -205,13 +204,13 @@ class ClockSampler:
         stop.set()
         th.join()
         t1 = time.perf_counter()
-        late = [s for s in samples if s[0] >= t0 + 0.25 * (t1 - t0)]
+        late = [x for x in samples if x[0] >= t0 + 1.0]
         clk = sorted(c for _, c, _ in late if c)
         pw = sorted(p for _, _, p in late if p)
         if not clk:
             return None
-        return {"clock_MHz": clk[len(clk) // 2], "power_W": pw[len(pw) // 2] if pw else None,
-                "samples": len(late), "launches": n, "seconds": round(t1 - t0, 2)}
+        return {"clock_MHz": round(clk[len(clk) // 2]), "power_W": pw[len(pw) // 2] if pw else None,
+                "launches": n, "seconds": round(t1 - t0, 2)}
 
 
 _CLOCK = None

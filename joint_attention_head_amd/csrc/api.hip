@@ -170,30 +170,40 @@ int32_t compute_units(int dev) {
 }
 
 // Persistent workgroups of a launch over nb query blocks of key_tiles key
-// tiles each, or 0 when it runs uncut.  setting: the caller's groups (0:
-// `cus` workgroups, cut only with at least two rounds of blocks and more
-// than 3% of the last round idle; > 0: that many, always cut; < 0: never).
-int64_t split_groups_for(int64_t nb, int64_t key_tiles, int32_t setting, int32_t cus) {
-  if (setting < 0 || nb < 1) return 0;
+// tiles each (groups == 0: the launch runs uncut), and the rounds of whole
+// blocks before the tail.  setting: the caller's groups (0: `cus`
+// workgroups, cut only with at least two rounds of blocks and more than 3%
+// of the last round idle; > 0: that many, always cut; < 0: never).
+struct SplitPlan {
+  int64_t groups = 0, whole = 0;
+};
+
+SplitPlan split_plan_for(int64_t nb, int64_t key_tiles, int32_t setting, int32_t cus) {
+  SplitPlan p;
+  if (setting < 0 || nb < 1) return p;
   int64_t groups = setting > 0 ? setting : cus;
-  if (groups < 2) return 0;
+  if (groups < 2) return p;
   if (setting == 0) {
     // fewer than two rounds: measured slower cut than whole (at one to two
     // rounds the shares stream keys out of step; with fewer blocks than
     // compute units the per-job start-up and the merges outweigh the idle
     // units: N = 1536 runs 19% (bf16) and 26% (fp8) slower cut)
-    if (nb < 2 * groups) return 0;
+    if (nb < 2 * groups) return p;
     // whole rounds, then a tail: cut when whole blocks would leave more
     // than 3% of the last round idle
     const int64_t rounds = (nb + groups - 1) / groups;
-    if (nb * 100 >= rounds * groups * 97) return 0;
+    if (nb * 100 >= rounds * groups * 97) return p;
   }
-  // every share holds at least one pair of the tail (the merge reads a slot
-  // of every share between a block's first and last)
-  const int64_t tail = nb >= 2 * groups ? nb - (nb / groups - 1) * groups : nb;
+  // all but the last one or two rounds whole; every share holds at least
+  // one pair of the tail (the merge reads a slot of every share between a
+  // block's first and last)
+  const int64_t whole = nb >= 2 * groups ? nb / groups - 1 : 0;
+  const int64_t tail = nb - whole * groups;
   groups = std::min<int64_t>(groups, tail * key_tiles);
-  if (groups < 2 || (setting == 0 && nb == groups)) return 0;
-  return groups;
+  if (groups < 2 || (setting == 0 && nb == groups)) return p;
+  p.groups = groups;
+  p.whole = whole;
+  return p;
 }
 
 // Split workspace layout: one arrival count per tail block (fewer than
@@ -232,13 +242,14 @@ fluxattn_status device_ok() {
   return ok ? FLUXATTN_OK : FLUXATTN_ERR_NO_DEVICE;
 }
 
+// Axis and frequency theta^(-2j/axes_a), in revolutions, of every pair.
 RopeTable make_rope_table(int32_t at, int32_t ah, int32_t aw, float theta) {
   RopeTable t;
   const int32_t dims[3] = {at, ah, aw};
   int pair = 0;
   for (int a = 0; a < 3; ++a)
     for (int j = 0; j < dims[a] / 2; ++j, ++pair) {
-      t.freq[pair] = static_cast<float>(pow(static_cast<double>(theta), -2.0 * j / dims[a]));
+      t.freq[pair] = static_cast<float>(pow(static_cast<double>(theta), -2.0 * j / dims[a]) / 6.283185307179586);
       t.axis[pair] = static_cast<int8_t>(a);
     }
   return t;
@@ -395,7 +406,8 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
     }
     cus = compute_units(d);
   }
-  const int64_t groups = split_groups_for(forward_grid_blocks(BH, N), forward_key_tiles(N), setting, cus);
+  const SplitPlan plan = split_plan_for(forward_grid_blocks(BH, N), forward_key_tiles(N), setting, cus);
+  const int64_t groups = plan.groups;
   if (need_out) {
     // validation only: report the workspace the launch needs
     *need_out = split_bytes(groups);
@@ -453,6 +465,7 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
     a.split_cnt = static_cast<int32_t *>(split->workspace);
     a.split_part = reinterpret_cast<float *>(static_cast<char *>(split->workspace) + kSplitCountBytes);
     a.split_groups = static_cast<int32_t>(groups);
+    a.split_whole = static_cast<int32_t>(plan.whole);
   }
   strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
               is_contiguous(o, H, N, D));
@@ -773,7 +786,7 @@ fluxattn_status fluxattn_split_workspace_bytes(int64_t B, int64_t H, int64_t N, 
     }
     cus = compute_units(d);
   }
-  *bytes = split_bytes(split_groups_for(forward_grid_blocks(B * H, N), forward_key_tiles(N), groups, cus));
+  *bytes = split_bytes(split_plan_for(forward_grid_blocks(B * H, N), forward_key_tiles(N), groups, cus).groups);
   return FLUXATTN_OK;
 }
 

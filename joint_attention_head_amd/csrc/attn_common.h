@@ -89,12 +89,13 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int total) {
 
 // ---- Key-range split.  Without a split, workgroup w computes query block
 // w whole (blocks in (b*h, query tile) order).  With split_groups = G
-// persistent workgroups and nb blocks, the first F = max(nb / G - 1, 0)
-// rounds go as whole blocks in launch order: workgroup w takes blocks w,
-// w + G, ..., so the workgroups running at one time work on neighbouring
-// blocks of the same heads and stream the same key tiles in step, sharing
-// them in L2.  The remaining blocks form the tail (fewer than 2G): its
-// (query block, key tile) pairs, key tiles in order inside each block, are
+// persistent workgroups and nb blocks, the first F = split_whole rounds
+// (chosen on the host, F G < nb) go as whole blocks in launch order:
+// workgroup w takes blocks w, w + G, ..., so the workgroups running at one
+// time work on neighbouring blocks of the same heads and stream the same
+// key tiles in step, sharing them in L2.  The remaining nb - F G blocks
+// form the tail: its (query block, key tile) pairs, key tiles in order
+// inside each block, are
 // dealt out as G equal contiguous shares, share w = pairs
 // [U w / G, U (w + 1) / G) of the tail's U to workgroup w.  A share spans
 // at most two tail blocks when it is shorter than a block, and then cuts
@@ -131,7 +132,7 @@ __device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows
   if (a.split_groups > 0) {
     const int G = a.split_groups;
     const int nb = a.BH * r.q_tiles;
-    r.whole = max(nb / G - 1, 0);
+    r.whole = a.split_whole;
     r.stride = G;
     r.base = r.whole * G;
     r.U = (int64_t)(nb - r.base) * r.key_tiles;

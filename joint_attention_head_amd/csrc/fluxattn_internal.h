@@ -12,7 +12,8 @@ constexpr int kHeadDim = 128;
 constexpr int kPairs = kHeadDim / 2;
 
 // Per head-dimension pair p (dims 2p, 2p+1): which position axis rotates it
-// and its fp32 frequency theta^(-2j/axes_a) (computed in fp64 on the host).
+// and its frequency theta^(-2j/axes_a) in revolutions (divided by 2 pi in
+// fp64 on the host, rounded to fp32).
 struct RopeTable {
   float freq[kPairs];
   int8_t axis[kPairs];
@@ -67,14 +68,15 @@ struct ForwardArgs {
   // (the key prologue's frequencies, in revolutions)
   float rope_rate[3][kPairs];
   // Key-range split (split_groups > 0): a persistent grid of split_groups
-  // workgroups, whole blocks first, then an equal contiguous share each of
-  // the remaining (query block, key tile) pairs.  A query block cut between
+  // workgroups, split_whole rounds of whole blocks first, then an equal
+  // contiguous share each of the remaining (query block, key tile) pairs.  A query block cut between
   // workgroups leaves one partial result per piece in split_part; the last
   // piece to finish merges them (split_cnt holds the arrival count of each
   // cut block and is left at zero).
   float *split_part;
   int32_t *split_cnt;
   int32_t split_groups;
+  int32_t split_whole;      // rounds of whole blocks before the tail
 };
 
 // Partial result of one piece of a split query block: per thread of the
