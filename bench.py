@@ -19,6 +19,8 @@ attention kernel's roofline fraction (its own mean launch time from HIP
 events on the launch stream; median and minimum beside it), the sustained
 graphics clock and power over a second of back-to-back launches (amdsmi),
 the prologue's GB/s warm and with the MALL flushed before every launch,
+the matrix cores' MFMA-only rate on the same shapes under "mfma_ceiling"
+(fluxattn_probe_mfma, with clock and power) and each kernel's fraction of it,
 the same figures at N=4608 (FLUX-dev 1024x1024)
 under "also", the fp8 path (E4M3 Q/K/V, fp8 matrix cores) on the 2048x2048
 image-to-image workload (B=1, H=24, N = 512 + 2 x 128x128 = 33280) under
@@ -135,6 +137,8 @@ def parse():
                    help="key-range split of the attention launches: 0 = one workgroup per compute unit, "
                         "cut where that balances the last round (default); < 0 = never cut; "
                         "> 0 = that many workgroups")
+    p.add_argument("--no-mfma-ceiling", dest="mfma_ceiling", action="store_false",
+                   help="skip the matrix-core ceiling (MFMA-only probe kernel, bf16 and fp8)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
@@ -223,14 +227,15 @@ def clock_sampler():
     return _CLOCK
 
 
-def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int = 0, clock: bool = False):
+def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int = 0, clock: bool = False,
+            inputs=None):
     import torch
 
     import joint_attention_head_amd as fa
     from workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[name]
-    inp = make_inputs(w)
+    inp = make_inputs(WORKLOADS[name]) if inputs is None else inputs
+    w = inp.workload
     fp8 = w.dtype == "fp8"
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
@@ -334,6 +339,35 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
         del sq, sk, sv, sqn, skn
     torch.cuda.empty_cache()
     return res
+
+
+def mfma_ceiling(kind: str, clock: bool):
+    """The matrix cores' sustained rate on the attention kernels' MFMA shape
+    with nothing else running (fluxattn_probe_mfma: two waves per SIMD,
+    back-to-back MFMAs on changing pseudo-random register operands): 5
+    warm-up and 20 timed launches of about 6 ms, HIP events on the stream."""
+    import torch
+
+    import joint_attention_head_amd as fa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    iters = 20000 if kind == "bf16" else 10000
+    stream = torch.cuda.current_stream()
+    run = lambda: fa.fluxattn_probe_mfma(kind, iters, cus, sink, stream=stream)
+    for _ in range(5):
+        flops = run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(20):
+        run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / 20
+    peak = BF16_PEAK_TFLOPS if kind == "bf16" else FP8_PEAK_TFLOPS
+    tf = flops / t / 1e12
+    return {"kernel": f"probe_{kind}_kernel (32x32x{16 if kind == 'bf16' else 64} MFMA only)",
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4), "launch_ms": round(t * 1e3, 3),
+            "sustained": clock_sampler().during(run) if clock else None}
 
 
 def calibrate_copy():
@@ -477,6 +511,8 @@ def main():
         }
         print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.4f} ms; sustained {r['sustained']}",
               file=sys.stderr, flush=True)
+    main_rl = roofline(main_res, "bf16", args, BF16_PEAK_TFLOPS, "attn_fwd_kernel (bf16, %s)" % (
+        "fused query prologue" if args.path == "fused" else "plain"))
     all_configs = None
     if args.all_configs:
         from workloads import WORKLOADS
@@ -500,6 +536,33 @@ def main():
                 "split_workspace_bytes": r["split_workspace_bytes"],
             }
             print(f"bench: {name} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
+    extras = None
+    if args.all_configs:
+        # non-gating extras (timing only): ragged N, a reference-image stream
+        # at t = 1, and peaked scores (each query's own key dominates) that
+        # keep the running shift moving
+        from workloads import custom_workload, make_inputs, make_peaked_inputs, WORKLOADS
+        cases = {
+            "odd_333": make_inputs(custom_workload(1, 24, 77, (16, 16), name="odd_333")),
+            "ref_t1_1024": make_inputs(custom_workload(1, 24, 512, (32, 32), (32, 32), name="ref_t1_1024")),
+            "peaked_1024": make_peaked_inputs(WORKLOADS["flux_dev_1024"]),
+        }
+        extras = {}
+        for name, inp in cases.items():
+            r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups, inputs=inp)
+            w = r["workload"]
+            extras[name] = {"B": w.B, "H": w.H, "N": w.N, "dtype": w.dtype,
+                            "forward_ms_median": round(r["forward_ms_median"], 4),
+                            "forward_tflops": round(r["forward_tflops"], 2),
+                            "frac": round(r["forward_tflops"] / BF16_PEAK_TFLOPS, 4)}
+            print(f"bench: extra {name} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
+    ceiling = None
+    if args.mfma_ceiling:
+        ceiling = {k: mfma_ceiling(k, args.clock) for k in ("bf16", "fp8")}
+        print(f"bench: MFMA-only ceiling {ceiling}", file=sys.stderr, flush=True)
+        main_rl["frac_of_mfma_ceiling"] = round(main_rl["achieved"] / ceiling["bf16"]["tflops"], 4)
+        if fp8 is not None:
+            fp8["roofline"]["frac_of_mfma_ceiling"] = round(fp8["roofline"]["achieved"] / ceiling["fp8"]["tflops"], 4)
     if args.calibrate_copy:
         calibrate_copy()
     cpu = None
@@ -528,8 +591,7 @@ def main():
             "split": {"groups": args.groups, "workspace_bytes": main_res["split_workspace_bytes"]},
             "B": w.B, "H": w.H, "N": w.N, "head_dim": 128,
         },
-        "roofline": roofline(main_res, "bf16", args, BF16_PEAK_TFLOPS, "attn_fwd_kernel (bf16, %s)" % (
-            "fused query prologue" if args.path == "fused" else "plain")),
+        "roofline": main_rl,
         "prologue": {
             "kernel": "prologue_bf16_kernel (%s)" % ("keys only" if args.path == "fused" else "queries and keys"),
             "bound": "hbm",
@@ -543,6 +605,8 @@ def main():
         "also": also,
         "fp8": fp8,
         "all_configs": all_configs,
+        "extras": extras,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -70,6 +70,7 @@ EXPORTS = (
     "fluxattn_forward_fused_ex_fp8",
     "fluxattn_split_workspace_bytes",
     "fluxattn_forward_fused_noalloc_bf16",
+    "fluxattn_probe_mfma",
     "fluxattn_status_string",
     "fluxattn_last_hip_error",
     "fluxattn_version",
@@ -143,6 +144,7 @@ _SIGS = {
     "fluxattn_split_workspace_bytes": [_i64, _i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_uint64)],
     "fluxattn_forward_fused_noalloc_bf16": [_p, _L, _p, _L, _p, _L, _p, _L, _p, _S, _p, _i64, _i64, _i64, _i64,
                                             _i32, _i32, _i32, _f, _f, _f, _i32, _p],
+    "fluxattn_probe_mfma": [_i32, _i64, _i32, _p, ctypes.POINTER(ctypes.c_double), _p],
 }
 
 
@@ -717,3 +719,16 @@ def fluxattn_forward_fused_noalloc_bf16(q, k, v, q_norm_w, pos_ids, o, streams=(
         pos_ids.data_ptr(), B, H, N, D, axes[0], axes[1], axes[2], float(theta), float(eps),
         float(softmax_scale), int(groups), _stream(stream)))
     return o
+
+
+def fluxattn_probe_mfma(kind: str, iterations: int, workgroups: int, sink: torch.Tensor, stream=None) -> float:
+    """Enqueue the matrix-core probe (include/fluxattn_probe.h): kind "bf16"
+    or "fp8"; sink a float32 device tensor of at least workgroups * 8
+    elements.  Returns the launch's matrix flops (time it with events)."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < 8 * workgroups:
+        raise ValueError("sink needs workgroups * 8 elements")
+    flops = ctypes.c_double(0.0)
+    _check(lib().fluxattn_probe_mfma({"bf16": 0, "fp8": 1}[kind], int(iterations), int(workgroups),
+                                     sink.data_ptr(), ctypes.byref(flops), _stream(stream)))
+    return float(flops.value)

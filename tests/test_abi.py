@@ -9,15 +9,19 @@ import pytest
 
 import joint_attention_head_amd as fa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fluxattn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 OK, NULLP, SHAPE, ALIGN, ALIAS, NODEV, HIPERR, WORKSPACE = range(8)
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fluxattn_\w+)\s*\(", src)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fluxattn_\w+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
