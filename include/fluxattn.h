@@ -436,7 +436,8 @@ fluxattn_status fluxattn_split_workspace_bytes(
  *          scratch.
  *   Memory: each device this entry point runs on holds its own copy of the
  *          array until the process ends; the first call on a device looks
- *          it up and clears its arrival counts on `stream`.
+ *          it up and clears its arrival counts on `stream` (a caller that
+ *          captures graphs makes that first call before capturing).
  *   Threads: every call on one device shares that device's array, which
  *          keeps the last call's partial results; calls that overlap in
  *          time on one device race (one stream, or order them by events).
