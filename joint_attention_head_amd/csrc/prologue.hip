@@ -267,9 +267,17 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
     const float *wp = (which ? a.w_k : a.w_q) + sid * kHeadDim;
     const float *s_in = which ? a.k_scale : a.q_scale;
     const float inv_out = 1.0f / (which ? sk : sq);
-    float w[16];
+    // weights times the rotation of each of the lane's pairs (even dim e,
+    // odd dim o): out_e = u w_e cos - v w_o sin, out_o = u w_e sin + v w_o cos
+    float ra[8], rb[8], rc[8], rd[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = wp[16 * c + i];
+    for (int i = 0; i < 8; ++i) {
+      const float we = wp[16 * c + 2 * i], wo = wp[16 * c + 2 * i + 1];
+      ra[i] = we * cs[i];
+      rb[i] = wo * sn[i];
+      rc[i] = we * sn[i];
+      rd[i] = wo * cs[i];
+    }
 
     const int64_t tin = (int64_t)tok * si.n + 16 * c, tout = (int64_t)tok * so.n + 16 * c;
     HeadWalk walk;
@@ -303,20 +311,26 @@ __global__ __launch_bounds__(kThreads) void prologue_fp8_kernel(PrologueArgs a, 
         e4m3x4_to_f32(x[u].y, f + 4);
         e4m3x4_to_f32(x[u].z, f + 8);
         e4m3x4_to_f32(x[u].w, f + 12);
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          f[i] *= s[u];
-          ss = fmaf(f[i], f[i], ss);
-        }
-        ss = row8_sum(ss);
-        const float rstd = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+        // The row is s * codes: its sum of squares is s^2 times that of the
+        // codes, and x w rstd = codes w (s rstd), so the dequantisation
+        // scale and the output scale meet in one factor g per row.
+        float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float uu = f[2 * i] * w[2 * i] * rstd;
-          const float vv = f[2 * i + 1] * w[2 * i + 1] * rstd;
-          f[2 * i] = fminf(fmaxf((uu * cs[i] - vv * sn[i]) * inv_out, -448.f), 448.f);
-          f[2 * i + 1] = fminf(fmaxf((uu * sn[i] + vv * cs[i]) * inv_out, -448.f), 448.f);
+          ss0 = fmaf(f[2 * i], f[2 * i], ss0);
+          ss1 = fmaf(f[2 * i + 1], f[2 * i + 1], ss1);
+        }
+        const float ss = row8_sum(ss0 + ss1);
+        const float su = s[u];
+        const float g = su * __builtin_amdgcn_rsqf((su * su) * ss * (1.0f / kHeadDim) + a.eps) * inv_out;
+        // |out| <= sqrt(D) max|w| / s_out = 448 up to fp32 rounding, and the
+        // conversion rounds everything below 464 to 448: no clamp.  (eps = 0
+        // with an all-zero row gives 0/0 = NaN, as in the bf16 path.)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float uu = f[2 * i] * g, vv = f[2 * i + 1] * g;
+          f[2 * i] = fmaf(uu, ra[i], -vv * rb[i]);
+          f[2 * i + 1] = fmaf(uu, rc[i], vv * rd[i]);
         }
         uint4 y;
         y.x = f32x4_to_e4m3(f);

@@ -151,6 +151,34 @@ def test_prologue_fp8_parity(case):
         assert np.abs(got).max() <= 448 * float(s_out.max()) + 1e-6
 
 
+def test_prologue_fp8_rows_at_the_bound():
+    """Rows whose whole energy sits in one dim, with unit weights, position 0
+    (no rotation) and eps = 0, normalise to exactly +-sqrt(D) max|w|, which
+    the output scale sqrt(D) max|w| / 448 maps to +-448: the largest finite
+    E4M3 value.  Every such code must come out as +-448 (0x7e / 0xfe), never
+    NaN, whatever the fp32 rounding of the factors on the way."""
+    _flush("prologue fp8 rows at the output bound")
+    B, H, N, D = 1, 3, 96, 128
+    k = torch.zeros(B, H, N, D)
+    rows = torch.arange(N)
+    dims = (7 * rows + 3) % D                        # even and odd dims, every pair
+    codes = torch.tensor([192.0, -448.0, 0.5, -2.0 ** -6, 26.0, -3.25])
+    for h in range(H):
+        k[0, h, rows, dims] = codes[(rows + h) % len(codes)]
+    k8 = k.to(torch.float8_e4m3fn)
+    ks = torch.tensor([[0.5, 3.0, 1e-3]])
+    w = torch.ones(D)
+    pos = torch.zeros(N, 3, dtype=torch.int32)
+    _, ko, _, sko = fa.fluxattn_qk_norm_rope_fp8(None, dev(k8), None, dev(ks), None, dev(w), dev(pos), eps=0.0)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(float(sko[0, 0]), math.sqrt(D) / 448.0, rtol=1e-6)
+    got = ko.cpu().view(torch.uint8)
+    want = torch.where(k8.view(torch.uint8) == 0, 0, torch.where(k < 0, 0xFE, 0x7E)).to(torch.uint8)
+    bad = int((got != want).sum())
+    _flush(f"  codes off the bound: {bad}")
+    assert bad == 0
+
+
 # ------------------------------------------------------------------ forward
 
 def run_forward_bf16(inp, **kw):
