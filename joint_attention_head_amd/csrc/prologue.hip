@@ -200,7 +200,7 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(const float *f) {
 // fp8 rows are 128 B: 8 lanes per token, 16 codes (8 rotation pairs) per
 // lane, so every lane moves 16 bytes per load and store; 32 tokens per block.
 // The (b,h) rows are split over grid.y in chunks of a.bh_chunk (sized on
-// the host for about eight blocks per compute unit), which gives the
+// the host for about twelve blocks per compute unit), which gives the
 // half-size fp8 stream enough blocks in flight.
 constexpr int kLanes8 = 8;
 constexpr int kTokensPerBlock8 = kThreads / kLanes8;
@@ -367,7 +367,7 @@ hipError_t launch_prologue_bf16(const PrologueArgs &a, const RopeTable &t, hipSt
 hipError_t launch_prologue_fp8(const PrologueArgs &a, const RopeTable &t, hipStream_t s) {
   PrologueArgs b = a;
   const int64_t bx = (a.N + kTokensPerBlock8 - 1) / kTokensPerBlock8;
-  b.bh_chunk = bh_chunk_for(a.BH, bx, 2048);   // the half-size fp8 stream: eight per compute unit
+  b.bh_chunk = bh_chunk_for(a.BH, bx, 3072);   // the half-size fp8 stream: about twelve per compute unit
   const dim3 grid((unsigned)bx, (unsigned)((a.BH + b.bh_chunk - 1) / b.bh_chunk));
   hipLaunchKernelGGL(prologue_fp8_kernel, grid, dim3(kThreads), 0, s, b, t);
   return hipGetLastError();
