@@ -342,18 +342,20 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
 
 
 def mfma_ceiling(kind: str, clock: bool):
-    """The matrix cores' sustained rate on the attention kernels' MFMA shape
-    with nothing else running (fluxattn_probe_mfma: two waves per SIMD,
-    back-to-back MFMAs on changing pseudo-random register operands): 5
-    warm-up and 20 timed launches of about 6 ms, HIP events on the stream."""
+    """The matrix cores' sustained rate on the attention kernel's MFMA shape
+    (bf16: 16x16x32, fp8: 32x32x64) with nothing else running
+    (fluxattn_probe_mfma: two waves per SIMD, back-to-back MFMAs on changing
+    pseudo-random register operands): 5 warm-up and 20 timed launches of
+    about 3-6 ms, HIP events on the stream."""
     import torch
 
     import joint_attention_head_amd as fa
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
-    iters = 20000 if kind == "bf16" else 10000
+    probe = "bf16_16x16x32" if kind == "bf16" else "fp8"
+    iters = 10000
     stream = torch.cuda.current_stream()
-    run = lambda: fa.fluxattn_probe_mfma(kind, iters, cus, sink, stream=stream)
+    run = lambda: fa.fluxattn_probe_mfma(probe, iters, cus, sink, stream=stream)
     for _ in range(5):
         flops = run()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -365,7 +367,8 @@ def mfma_ceiling(kind: str, clock: bool):
     t = ev[0].elapsed_time(ev[1]) * 1e-3 / 20
     peak = BF16_PEAK_TFLOPS if kind == "bf16" else FP8_PEAK_TFLOPS
     tf = flops / t / 1e12
-    return {"kernel": f"probe_{kind}_kernel (32x32x{16 if kind == 'bf16' else 64} MFMA only)",
+    shape = "16x16x32" if kind == "bf16" else "32x32x64"
+    return {"kernel": f"fluxattn_probe_mfma ({kind} {shape} MFMA only, the attention kernel's shape)",
             "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4), "launch_ms": round(t * 1e3, 3),
             "sustained": clock_sampler().during(run) if clock else None}
 

@@ -429,7 +429,7 @@ fluxattn_status fluxattn_split_workspace_bytes(
  * (fluxattn_split.groups) whose workspace is a static array of the library
  * instead of caller memory: for callers that cannot allocate device memory
  * (code under HIP graph capture, serving loops, harnesses that forbid it).
- *   Limit: a split of at most 256 workgroups (66.1 MiB, one per compute unit
+ *   Limit: a split of at most 256 workgroups (68.1 MiB, one per compute unit
  *          of an MI355X, the default setting's launch there); a launch
  *          whose split would need more returns FLUXATTN_ERR_WORKSPACE
  *          before anything is enqueued.  Launches that are not cut use no

@@ -723,12 +723,13 @@ def fluxattn_forward_fused_noalloc_bf16(q, k, v, q_norm_w, pos_ids, o, streams=(
 
 def fluxattn_probe_mfma(kind: str, iterations: int, workgroups: int, sink: torch.Tensor, stream=None) -> float:
     """Enqueue the matrix-core probe (include/fluxattn_probe.h): kind "bf16"
-    or "fp8"; sink a float32 device tensor of at least workgroups * 8
-    elements.  Returns the launch's matrix flops (time it with events)."""
+    (32x32x16), "fp8" (32x32x64) or "bf16_16x16x32"; sink a float32 device
+    tensor of at least workgroups * 8 elements.  Returns the launch's matrix
+    flops (time it with events)."""
     _need(sink, "sink", torch.float32)
     if sink.numel() < 8 * workgroups:
         raise ValueError("sink needs workgroups * 8 elements")
     flops = ctypes.c_double(0.0)
-    _check(lib().fluxattn_probe_mfma({"bf16": 0, "fp8": 1}[kind], int(iterations), int(workgroups),
+    _check(lib().fluxattn_probe_mfma({"bf16": 0, "fp8": 1, "bf16_16x16x32": 2}[kind], int(iterations), int(workgroups),
                                      sink.data_ptr(), ctypes.byref(flops), _stream(stream)))
     return float(flops.value)

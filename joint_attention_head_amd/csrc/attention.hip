@@ -8,21 +8,28 @@
 //
 // Design (flash-style single pass over K/V; scores never leave registers):
 //
-//  * Workgroup = 8 waves = 256 query rows of one (b,h); wave w owns 32 rows.
-//    Queries stay in VGPRs as the B operand of v_mfma_f32_32x32x16_bf16 and
-//    each wave computes the transposed score tile S^T = K Q^T, so a lane owns
-//    one query (lane % 32) and 16 of every 32 keys: the softmax row state is
-//    lane-local up to one exchange with lane ^ 32.
-//  * O^T = V^T P^T takes the probabilities straight from registers as the B
-//    operand.  The keys a lane holds for one MFMA step are
-//    {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); since keys are summed over,
-//    the V^T operand only has to list the same keys in the same order.  V
-//    tiles sit in LDS as they are in memory (row = key); two transposing
-//    reads (ds_read_b64_tr_b16) give a lane those 8 keys at its head dim.
+//  * Workgroup = 8 waves = 256 query rows of one (b,h); wave w owns 32 rows
+//    as two halves of 16 (h = 0, 1).  Every product is a
+//    v_mfma_f32_16x16x32_bf16: at the chip's power limit it sustains a
+//    higher clock than the 32x32x16 shape, which moves more accumulator and
+//    operand register bytes per flop.  Lane l works on query l % 16 of each
+//    half, and on k-slots 8 g .. +8 and output rows 4 g .. +4 of every
+//    MFMA, g = l / 16.
+//  * S^T = K Q^T: K (16 keys x 32 dims) is the A operand, read from LDS
+//    with one ds_read_b128 per lane, and the queries stay in VGPRs as the B
+//    operand.  Lane l then holds, for each of its two queries, keys
+//    16 kb + 4 g .. +4 of every 16-key block kb: the row state of a query
+//    is spread over the four lanes l % 16 + 16 g.
+//  * O^T = V^T P^T takes the probabilities straight from registers as the
+//    B operand: of a 32-key block the lane's own keys {4 g .. +4} and
+//    {16 + 4 g .. +4} fill its k-slots 8 g .. +8.  Since keys are summed
+//    over, the V^T operand only has to list the same keys in the same
+//    k-slots; two transposing reads (ds_read_b64_tr_b16) of the V tile, as
+//    it is in memory (row = key), give a lane those 8 keys at its head dim.
 //  * Ping-pong: the waves form two groups of four, one wave of each group per
 //    SIMD.  Every phase ends with a workgroup barrier; in each phase one
 //    group runs its matrix half-step (PV of the current tile, QK^T of the
-//    next one: 32 MFMAs, at raised wave priority) while the other runs its
+//    next one: 64 MFMAs, at raised wave priority) while the other runs its
 //    vector half-step (online softmax of the next tile), so the matrix cores
 //    and the VALU of every SIMD are busy at the same time.
 //  * The matrix half-step issues no VALU instruction: a VALU op of the MFMA
@@ -40,11 +47,11 @@
 //    row's running shift), then p = 2^x.  The plain form spends one FMA per
 //    score on x; the fused form gets it from the MFMA, with c folded into
 //    the queries and -b as the accumulator's initial value.  The row
-//    maximum is only scanned when the tile's row sum (an upper bound of
-//    every probability in it) exceeds 2^16; b then moves up to the maximum
-//    if that exceeds it by more than 8, with O and l rescaled.  O / l is
-//    unchanged by the shift.  l sums the fp32 probabilities; P is rounded
-//    to bf16 for the MFMA.
+//    maximum is only scanned when a lane's share of the tile's row sum (an
+//    upper bound of every probability in it) exceeds 2^16; b then moves up
+//    to the maximum if that exceeds it by more than 8, with O and l
+//    rescaled.  O / l is unchanged by the shift.  l sums the fp32
+//    probabilities; P is rounded to bf16 for the MFMA.
 //  * blockIdx is remapped so that the workgroups the dispatcher sends to one
 //    XCD (blockIdx % 8) take consecutive query tiles of the same (b,h) and
 //    share its K/V stream through that XCD's L2.
@@ -78,79 +85,103 @@ using namespace attn;
 //  K tile: row = key (256 B), 16-byte chunk c of the head dim stored at
 //          c ^ (key & 15): the 16 keys one ds_read_b128 phase touches hit 16
 //          distinct bank groups.
-//  V tile: row = key (256 B), chunk c stored at c ^ vsw(key), vsw taking
-//          key % 4 to 0, 6, 10, 12.  A transposing read touches 4
-//          consecutive keys x 32 bytes per 16 lanes and 8 keys x 64 bytes per
-//          wave; the swizzle puts every 32-byte piece of one 256-byte bank
-//          row in its own banks.  The swizzle only moves chunks within bits
-//          1..3 of their index and depends on key % 4, so key offsets that
-//          are multiples of 4 stay immediates.
+//  V tile: row = key (256 B), chunk c stored at c ^ vsw(key), vsw(key) =
+//          2 (key % 8).  A transposing read touches 4 consecutive keys x 32
+//          bytes (two chunks) per 16 lanes and 8 keys x 32 bytes per half
+//          wave; the swizzle puts those eight 32-byte pieces in the eight
+//          32-byte bank windows of a 256-byte bank row.  It depends on
+//          key % 8 only, so key offsets that are multiples of 8 stay
+//          immediates.
 __device__ __forceinline__ int k_off(int key, int ch) { return key * 256 + ((ch ^ (key & 15)) << 4); }
-__device__ __forceinline__ int vsw(int key) { return (0xCA60 >> (4 * (key & 3))) & 15; }
+__device__ __forceinline__ int vsw(int key) { return (key & 7) << 1; }
 __device__ __forceinline__ int v_off(int key, int ch) { return key * 256 + ((ch ^ vsw(key)) << 4); }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const char *p) {
   return *reinterpret_cast<const bf16x8_t *>(p);
 }
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-// two transposing reads: elements 0..3 from p, 4..7 from p + 2048 (8 keys on)
+// two transposing reads: elements 0..3 from p, 4..7 from p + 4096 (16 keys on)
 __device__ __forceinline__ bf16x8_t lds_read_tr2(const char *p) {
   typedef __attribute__((address_space(3))) i16x4_t *lp;
   const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
-  const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 2048));
+  const i16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 4096));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// D = C + A B, 16 x 16 x 32, bf16 operands, fp32 accumulation.
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x combined over the four lanes l % 16 + 16 g that hold one query (max or
+// sum; the same value, bit for bit, in all four: each step combines a
+// pair of lanes commutatively)
+__device__ __forceinline__ float quad_max(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
 // Queries of the fused entry points: raw Q -> RMSNorm over the 128 dims ->
 // rotation of each adjacent pair by its axis position times frequency
-// (the prologue's operations, on the 64 dims this lane holds:
-// 16 kk + 8 hi + i; the other 64 are in lane ^ 32) -> times c = softmax
-// scale * log2 e -> bf16, so that the QK^T MFMA yields base-2 logits.  The
-// one bf16 rounding of Q' is the same as the prologue's, applied to c Q'.
-__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[8], const ForwardArgs &a, const RopeLds *rope,
-                                             const HeadView &vq, int q_row, int hi) {
+// (the prologue's operations) -> times c = softmax scale * log2 e -> bf16,
+// so that the QK^T MFMA yields base-2 logits.  The lane holds two queries
+// (q_row[h], h = 0, 1) and of each the dims 32 ks + 8 g .. +8 (ks = 0..3):
+// the other 96 dims of a query are in lanes lane ^ 16, ^ 32, ^ 48.  The one
+// bf16 rounding of Q' is the same as the prologue's, applied to c Q'.
+__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[2][4], const ForwardArgs &a, const RopeLds *rope,
+                                             const HeadView &vq, const int (&q_row)[2], int g) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
-    qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-  }
-  float ss = 0.f;
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = (float)qf[kk][i];
-      ss = fmaf(x, x, ss);
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t off = (uint32_t)q_row[h] * vq.row + (uint32_t)((32 * ks + 8 * g) * 2);
+      qf[h][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(ss), __float_as_int(ss), false, false);
-    ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
-  }
-  // rstd and the logit scale c folded into the weights: Q' c = (x w rstd c)
-  // rotated
-  const float rs = a.scale_log2 / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
-  // position ids of this query (rows past N belong to no token: any valid
-  // row serves, their outputs are never stored)
-  const int tok = min(q_row, a.N - 1);
-  const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
-  const float *w_q = stream_weights(a, tok);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    float x[8];
+  for (int h = 0; h < 2; ++h) {
+    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)qf[kk][i];
-    const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi);
-    const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 16 * kk + 8 * hi + 4);
-    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float sn[4], cs[4];
-    rotations4(rope, pf, 8 * kk + 4 * hi, sn, cs);   // pairs 8 kk + 4 hi + m
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float u = x[2 * m] * (w[2 * m] * rs);
-      const float v = x[2 * m + 1] * (w[2 * m + 1] * rs);
-      qf[kk][2 * m] = (__bf16)(u * cs[m] - v * sn[m]);
-      qf[kk][2 * m + 1] = (__bf16)(u * sn[m] + v * cs[m]);
+      for (int i = 0; i < 8; ++i) {
+        const float x = (float)qf[h][ks][i];
+        ss = fmaf(x, x, ss);
+      }
+    ss = quad_sum(ss);   // all 128 dims of this query
+    // rstd and the logit scale c folded into the weights: Q' c = (x w rstd c)
+    // rotated
+    const float rs = a.scale_log2 / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+    // position ids of this query (rows past N belong to no token: any valid
+    // row serves, their outputs are never stored)
+    const int tok = min(q_row[h], a.N - 1);
+    const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
+    const float *w_q = stream_weights(a, tok);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)qf[h][ks][i];
+      const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g);
+      const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g + 4);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float sn[4], cs[4];
+      rotations4(rope, pf, 16 * ks + 4 * g, sn, cs);   // pairs 16 ks + 4 g + m
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float u = x[2 * m] * (w[2 * m] * rs);
+        const float v = x[2 * m + 1] * (w[2 * m + 1] * rs);
+        qf[h][ks][2 * m] = (__bf16)(u * cs[m] - v * sn[m]);
+        qf[h][ks][2 * m + 1] = (__bf16)(u * sn[m] + v * cs[m]);
+      }
     }
   }
 }
@@ -163,7 +194,7 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   // overlap the fused query transform's temporaries)
   int tid = tid_in;
   asm volatile("" : "+v"(tid));
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int N = a.N;
   // wave-uniform job fields (they address the scalar buffer descriptors)
   const int bh = __builtin_amdgcn_readfirstlane(job.bh), qt = __builtin_amdgcn_readfirstlane(job.qt);
@@ -171,19 +202,22 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
 
   // ---- per-head base pointers, token-row pitches and buffer extents
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 2, bh, a.H, N);
-  // ---- queries: qf[kk] = Q[q][16kk + 8hi .. +8), q = this lane's row
-  // (first, so the fused transform's temporaries overlap no other state)
-  const int q_row = qt * kBR + wave * 32 + l32;
-  bf16x8_t qf[8];
+  // ---- queries: qf[h][ks] = Q[q_row[h]][32 ks + 8 g .. +8), the B
+  // operands of QK^T (first, so the fused transform's temporaries overlap
+  // no other state)
+  const int q_row[2] = {qt * kBR + wave * 32 + l16, qt * kBR + wave * 32 + 16 + l16};
+  bf16x8_t qf[2][4];
   if constexpr (FUSEQ) {
-    load_q_fused(qf, a, rope, vq, q_row, hi);
+    load_q_fused(qf, a, rope, vq, q_row, g);
   } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t off = (uint32_t)q_row * vq.row + (uint32_t)((16 * kk + 8 * hi) * 2);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t off = (uint32_t)q_row[h] * vq.row + (uint32_t)((32 * ks + 8 * g) * 2);
+        qf[h][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      }
   }
 
   const HeadView vk = head_view<STRIDED>(a.k, a.sk, 2, bh, a.H, N);
@@ -215,24 +249,24 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
     const int row = 32 * group + 8 * gw + 4 * i + (lane >> 4);
     v_dgoff[i] = (uint32_t)row * vv.row + (uint32_t)(16 * ((lane & 15) ^ vsw(row)));
   }
-  //  MFMA fragments: K (kk) row l32, chunk 2 kk + hi; slot and 32-key
-  //     block are immediates.
-  uint32_t kf[8], vtr[4];
+  //  QK^T fragments (A operand): K row l16 (+ 16 kb: immediate), chunk
+  //     4 ks + g, i.e. dims 32 ks + 8 g .. +8; the slot is an immediate.
+  uint32_t kf[4], vtr[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kf[kk] = (uint32_t)k_off(l32, 2 * kk + hi);
-  //  PV operand by transposing reads.  Within 16 lanes, lane m of a
-  //     ds_read_b64_tr_b16 receives element m % 4 of the 8-byte pieces that
-  //     lanes m / 4, 4 + m / 4, 8 + m / 4, 12 + m / 4 address.  Lane L
-  //     addresses key 4 (L / 32) + (L / 4) % 4 (+ 16 st + 8 half: slot and
-  //     key offsets are immediates), head dims 32 db + 16 ((L / 16) % 2) +
-  //     4 (L % 4) .. +4; so lane l receives head dim 32 db + l % 32 of keys
-  //     16 st + 8 half + 4 (l / 32) + 0..3, the order of the B operand.
+  for (int ks = 0; ks < 4; ++ks) kf[ks] = (uint32_t)k_off(l16, 4 * ks + g);
+  //  PV fragments (A operand, V^T) by transposing reads.  Within 16 lanes,
+  //     lane m of a ds_read_b64_tr_b16 receives element m % 4 of the 8-byte
+  //     pieces that lanes m / 4, 4 + m / 4, 8 + m / 4, 12 + m / 4 address.
+  //     Lane L addresses key 4 (L / 16) + (L / 4) % 4 (+ 32 kb + 16 t: the
+  //     32-key block and the read, immediates), head dims 16 db + 4 (L % 4)
+  //     .. +4; so lane l receives head dim 16 db + l % 16 of keys
+  //     32 kb + 16 t + 4 g + 0..3, its k-slots 8 g + 4 t .. +4.
   {
-    const int row0 = 4 * hi + ((lane >> 2) & 3);
-    const int dh = (lane >> 4) & 1, i4 = lane & 3;
+    const int row0 = 4 * g + ((lane >> 2) & 3);
+    const int i4 = lane & 3;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      vtr[db] = (uint32_t)(kVRingOffset + v_off(row0, 4 * db + 2 * dh + (i4 >> 1)) + 8 * (i4 & 1));
+    for (int db = 0; db < 8; ++db)
+      vtr[db] = (uint32_t)(kVRingOffset + v_off(row0, 2 * db + (i4 >> 1)) + 8 * (i4 & 1));
   }
 
   // ---- ring traffic helpers
@@ -270,140 +304,154 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  f32x16_t o[4];
+  // Accumulators, [.. + h] for the lane's query of half h:
+  //  o[2 db + h]: O^T head dims 16 db + 4 g .. +4;
+  //  s[2 kb + h]: S^T keys 16 kb + 4 g .. +4 of the tile (kb = 0..3);
+  //  pf[2 kb + h]: P^T operand of 32-key block kb (kb = 0, 1): keys
+  //      32 kb + 4 g .. +4, then 32 kb + 16 + 4 g .. +4.
+  f32x4_t o[16];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  f32x16_t s[2];
+  for (int i = 0; i < 16; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t s[8];
   bf16x8_t pf[4];
-  float b_run = 0.f;      // this row's running shift, base-2 units
-  f32x16_t bias = {};     // fused: -b_run in every element
-  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-  const f32x16_t zero = {};
+  float b_run[2] = {0.f, 0.f};        // the rows' running shifts, base-2 units
+  f32x4_t bias[2] = {};               // fused: -b_run[h] in every element
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};   // [2 kb + h]: this lane's keys
+  const f32x4_t zero = {};
 
-  // Matrix half-step as a 32-step software pipeline over operand fragments:
-  // steps 0..15 are PV of the current tile (16-key step st = s/4, head-dim
-  // block db = s%4), steps 16..31 QK^T of the next tile (kk = (s-16)/2,
-  // 32-key block kb = (s-16)%2).  Fragment s+kPre is requested from LDS
-  // before MFMA s is issued, and scheduling fences keep that order.  The
-  // V tile of the PV steps is complete before the half-step starts, so the
-  // first kPre fragments are requested before the barrier.  A PV fragment
-  // is two transposing reads, a QK^T fragment one ds_read_b128.
+  // Matrix half-step as a 32-step software pipeline over operand fragments,
+  // each serving the MFMAs of both query halves: steps 0..15 are PV of the
+  // current tile (32-key block kb = s/8, head-dim block db = s%8), steps
+  // 16..31 QK^T of the next tile (dims 32 ks, ks = (s-16)/4, 16-key block
+  // kb = (s-16)%4: eight accumulator chains in turn).  Fragment s+kPre is
+  // requested from LDS before the MFMAs of step s are issued, and
+  // scheduling fences keep that order.  The V tile of the PV steps is
+  // complete before the half-step starts, so the first kPre fragments are
+  // requested before the barrier.  A PV fragment is two transposing reads,
+  // a QK^T fragment one ds_read_b128.
   constexpr int kPre = 6;
   auto frag = [&](int step, int kslot_bytes, int vslot_bytes) __attribute__((always_inline)) -> bf16x8_t {
     if (step >= 16) {
-      const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
-      return lds_read_b128(lds + kf[kk] + (kslot_bytes + kb * 32 * 256));
+      const int ks = (step - 16) >> 2, kb = (step - 16) & 3;
+      return lds_read_b128(lds + kf[ks] + (kslot_bytes + kb * 16 * 256));
     }
-    const int st = step >> 2, db = step & 3;
-    return lds_read_tr2(lds + vtr[db] + (vslot_bytes + st * 16 * 256));
+    const int kb = step >> 3, db = step & 7;
+    return lds_read_tr2(lds + vtr[db] + (vslot_bytes + kb * 32 * 256));
   };
   auto matrix_step = [&](int step, bf16x8_t f) __attribute__((always_inline)) {
     if (step >= 16) {
-      const int kk = (step - 16) >> 1, kb = (step - 16) & 1;
+      const int ks = (step - 16) >> 2, kb = (step - 16) & 3;
       // fused: Q' carries c and the accumulator starts at -b
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk ? s[kb] : (FUSEQ ? bias : zero), 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s[2 * kb + h] = mfma16(f, qf[h][ks], ks ? s[2 * kb + h] : (FUSEQ ? bias[h] : zero));
     } else {
-      const int st = step >> 2, db = step & 3;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[st], o[db], 0, 0, 0);
+      const int kb = step >> 3, db = step & 7;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) o[2 * db + h] = mfma16(f, pf[2 * kb + h], o[2 * db + h]);
     }
   };
 
-  // Online softmax of tile j.  Lane owns query l32 and keys
-  // 32 kb + 8 (r / 4) + 4 hi + r % 4 of the tile (register r of s[kb]);
-  // x = c*S - b (c = softmax scale * log2 e) by one FMA per score, or
-  // straight from the MFMA in the fused form.  Common case: p = 2^x
-  // straight away; the row maximum is
-  // only needed when some p may be large, which the tile's own row sum
-  // (>= every p in it) tells.  Then, or on the first tile, b moves up to the
-  // row maximum when that exceeds it by more than 8 (first tile: moves to
-  // it), O and l are scaled by 2^-shift and p recomputed, so p <= 2^16
-  // always and O / l is unchanged.
+  // Online softmax of tile j.  The lane holds, for query h, keys
+  // 16 kb + 4 g + r of the tile in register r of s[2 kb + h]; x = c*S - b
+  // (c = softmax scale * log2 e) by one FMA per score, or straight from the
+  // MFMA in the fused form.  Common case: p = 2^x straight away; the row
+  // maximum is only needed when some p may be large, which the lane's share
+  // of the tile's row sum (>= every p in it) tells.  Then, or on the first
+  // tile, b moves up to the row maximum (over the query's four lanes) when
+  // that exceeds it by more than 8 (first tile: moves to it), O and l are
+  // scaled by 2^-shift and p recomputed, so p <= 2^16 always and O / l is
+  // unchanged.
   auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value != 0;
     if constexpr (!FUSEQ) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c, -b_run);
+        for (int r = 0; r < 4; ++r) s[i][r] = fmaf(s[i][r], c, -b_run[i & 1]);
     }
     if ((kt0 + j) * kBC + kBC > N) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = (kt0 + j) * kBC + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N) s[kb][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = (kt0 + j) * kBC + 16 * (i >> 1) + 4 * g + r;
+          if (key >= N) s[i][r] = -INFINITY;
         }
     }
     float t[4];
     auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st >> 1, r0 = 8 * (st & 1);
-        float acc;   // starts at the first pair: 0 + x is not folded (-0)
-        bf16x8_t pv8;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(s[kb][r0 + i]);
-          const float e1 = __builtin_amdgcn_exp2f(s[kb][r0 + i + 1]);
-          acc = i ? acc + (e0 + e1) : e0 + e1;
-          pv8[i] = (__bf16)e0;
-          pv8[i + 1] = (__bf16)e1;
+        for (int h = 0; h < 2; ++h) {
+          float acc;   // starts at the first pair: 0 + x is not folded (-0)
+          bf16x8_t pv8;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int i = 2 * (2 * kb + half) + h;
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float e0 = __builtin_amdgcn_exp2f(s[i][r]);
+              const float e1 = __builtin_amdgcn_exp2f(s[i][r + 1]);
+              acc = (half || r) ? acc + (e0 + e1) : e0 + e1;
+              pv8[4 * half + r] = (__bf16)e0;
+              pv8[4 * half + r + 1] = (__bf16)e1;
+            }
+          }
+          t[2 * kb + h] = acc;
+          pf[2 * kb + h] = pv8;
         }
-        t[st] = acc;
-        pf[st] = pv8;
-      }
     };
     if constexpr (!kFirst) exps();
-    const float tot = (t[0] + t[1]) + (t[2] + t[3]);
-    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot <= 65536.f)) != 0) {
-      float mq[4];
+    const float tot0 = t[0] + t[2], tot1 = t[1] + t[3];
+    if (kFirst || __builtin_amdgcn_ballot_w64(!(tot0 <= 65536.f) || !(tot1 <= 65536.f)) != 0) {
+      float mx[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kb = g >> 1, r0 = 8 * (g & 1);
-        float m = fmaxf(s[kb][r0], s[kb][r0 + 1]);
+      for (int h = 0; h < 2; ++h) {
+        float mq[4];
 #pragma unroll
-        for (int r = 2; r < 8; ++r) m = fmaxf(m, s[kb][r0 + r]);
-        mq[g] = m;
+        for (int kb = 0; kb < 4; ++kb) {
+          const f32x4_t x = s[2 * kb + h];
+          mq[kb] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        }
+        mx[h] = quad_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
       }
-      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
-        mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over both half-waves
-      }
-      if (kFirst || __builtin_amdgcn_ballot_w64(mx > 8.0f) != 0) {
-        const float d = kFirst ? mx : fmaxf(mx, 0.f);
-        b_run += d;
-        if constexpr (FUSEQ) {
+      if (kFirst || __builtin_amdgcn_ballot_w64(mx[0] > 8.0f || mx[1] > 8.0f) != 0) {
+        float d[2];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) bias[i] = -b_run;
+        for (int h = 0; h < 2; ++h) {
+          d[h] = kFirst ? mx[h] : fmaxf(mx[h], 0.f);
+          b_run[h] += d[h];
+          if constexpr (FUSEQ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bias[h][e] = -b_run[h];
+          }
         }
         if constexpr (!kFirst) {
-          const float alpha = __builtin_amdgcn_exp2f(-d);
+          const float alpha[2] = {__builtin_amdgcn_exp2f(-d[0]), __builtin_amdgcn_exp2f(-d[1])};
 #pragma unroll
-          for (int g = 0; g < 4; ++g) l_part[g] *= alpha;
+          for (int i = 0; i < 4; ++i) l_part[i] *= alpha[i & 1];
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            for (int e = 0; e < 4; ++e) o[i][e] *= alpha[i & 1];
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][r] -= d;
+          for (int r = 0; r < 4; ++r) s[i][r] -= d[i & 1];
         exps();
       }
     }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) l_part[st] += t[st];
+    for (int i = 0; i < 4; ++i) l_part[i] += t[i];
     // keep the exponentials in this (vector) half-step: without these the
     // compiler sinks them next to their MFMA consumers in the matrix one
 #pragma unroll
-    for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(pf[st]));
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pf[i]));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(l_part[g]));
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(l_part[i]));
   };
 
   // Schedule of each wave: QK^T(0), vector half-step of tile 0, then per
@@ -482,25 +530,25 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (group == 0) __syncthreads();
 
-  // ---- epilogue: O / l, one bf16 rounding; lane holds query l32 and head
-  // dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end are dropped
-  float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_run), __float_as_int(l_run), false, false);
-    l_run = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // both half-waves' keys
-  }
+  // ---- epilogue: O / l, one bf16 rounding; the lane holds head dims
+  // 16 db + 4 g .. +4 of its two queries; stores past the head's end are
+  // dropped
+  float l_run[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) l_run[h] = quad_sum(l_part[h] + l_part[2 + h]);   // the query's four lanes
   // a piece of a split block: the piece that finishes second merges
-  if (job.cut >= 0 && !split_merge(a, job, o, b_run, l_run, tid, split_ticket)) return;
-  const float inv = 1.0f / l_run;
+  if (job.cut >= 0 && !split_merge<2>(a, job, o, b_run, l_run, tid, split_ticket)) return;
+  const float inv[2] = {1.0f / l_run[0], 1.0f / l_run[1]};
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t x = o[2 * db + h];
       u32x2_t w;
-      w[0] = pack_bf16(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-      w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-      const uint32_t off = (uint32_t)q_row * vo.row + (uint32_t)((32 * db + 8 * g + 4 * hi) * 2);
+      w[0] = pack_bf16(x[0] * inv[h], x[1] * inv[h]);
+      w[1] = pack_bf16(x[2] * inv[h], x[3] * inv[h]);
+      const uint32_t off = (uint32_t)q_row[h] * vo.row + (uint32_t)((16 * db + 4 * g) * 2);
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
     }
 }

@@ -534,10 +534,11 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
 
   // ---- epilogue: O * s_v / l, one bf16 rounding; lane holds query l32 and
   // head dims 32 db + 8 g + 4 hi + (0..3); stores past the head's end drop
-  float l_run = lsum[0];   // all 64 keys of every tile, rounded P
+  float l_run[1] = {lsum[0]};   // all 64 keys of every tile, rounded P
+  float b_fin[1] = {b_run};
   // a piece of a split block: the piece that finishes second merges
-  if (job.cut >= 0 && !split_merge(a, job, o, b_run, l_run, tid, split_ticket)) return;
-  const float inv = o_scale / l_run;
+  if (job.cut >= 0 && !split_merge<1>(a, job, o, b_fin, l_run, tid, split_ticket)) return;
+  const float inv = o_scale / l_run[0];
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(vo.base, vo.bytes);
 #pragma unroll
   for (int db = 0; db < 4; ++db)

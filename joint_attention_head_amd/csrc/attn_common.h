@@ -11,6 +11,7 @@ namespace attn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -217,12 +218,16 @@ __device__ __forceinline__ bool split_next(SplitRange &r, SplitJob &j) {
 
 // End of one piece of a cut block.  The piece stores its O accumulators
 // o (unnormalised, relative to 2^b: row shift b in base-2 units) and its
-// normaliser l in its slot, then counts itself in at the block.  All but
+// normalisers l in its slot, then counts itself in at the block.  All but
 // the last to arrive return false; the last reads the other pieces and
 // merges them into (o, b, l): every piece rescaled to the largest shift
 // and summed in share order (whichever piece merges, the result is the
 // same, bit for bit), resets the count for the next launch and returns
 // true (it then stores O).  Nobody waits for anybody.
+// A thread holds R query rows (1 or 2): its 64 accumulators are 16 float4
+// (acc4 below), float4 i belonging to row i % R, and b[r], l[r] are row r's
+// shift and normaliser.  Float4 i of every thread sits at i * 8 KiB (a
+// scalar offset) + 16 * thread.
 // Coherence between the workgroups (possibly on different XCDs, whose L2
 // caches are not coherent with each other) comes from device-scope
 // accesses to the partials and the count alone: the partial stores and
@@ -233,8 +238,23 @@ __device__ __forceinline__ bool split_next(SplitRange &r, SplitJob &j) {
 // threads of the workgroup call this; it contains two workgroup barriers.
 constexpr int kCPolDevice = 16;   // buffer cache policy: sc1 (device scope)
 
-__device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob &job, f32x16_t (&o)[4], float &b,
-                                            float &l, int tid, int *ticket) {
+// float4 i of a thread's 64 accumulators, held as 4 x 16 or as 16 x 4 floats
+__device__ __forceinline__ f32x4_t acc4(const f32x16_t (&o)[4], int i) {
+  const int db = i >> 2, g = i & 3;
+  return f32x4_t{o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+}
+__device__ __forceinline__ f32x4_t acc4(const f32x4_t (&o)[16], int i) { return o[i]; }
+__device__ __forceinline__ void acc4_set(f32x16_t (&o)[4], int i, f32x4_t v) {
+  const int db = i >> 2, g = i & 3;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[db][4 * g + e] = v[e];
+}
+__device__ __forceinline__ void acc4_set(f32x4_t (&o)[16], int i, f32x4_t v) { o[i] = v; }
+
+template <int R, class Acc>
+__device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob &job, Acc &o, float (&b)[R],
+                                            float (&l)[R], int tid, int *ticket) {
+  static_assert(R == 1 || R == 2, "one or two rows per thread");
   constexpr uint32_t kPieceBytes = (uint32_t)(kSplitPieceFloats * 4);
   constexpr uint32_t kBLOffset = 64u * 4u * kSplitThreads;
   auto slot_rsrc = [&](int slot) {
@@ -244,19 +264,16 @@ __device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob
   {
     const __amdgpu_buffer_rsrc_t mine = slot_rsrc(job.slot);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int db = i >> 2, g = i & 3;
-      u32x4_t w;
-      w[0] = __float_as_uint(o[db][4 * g + 0]);
-      w[1] = __float_as_uint(o[db][4 * g + 1]);
-      w[2] = __float_as_uint(o[db][4 * g + 2]);
-      w[3] = __float_as_uint(o[db][4 * g + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(w, mine, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
-    }
-    u32x2_t w;
-    w[0] = __float_as_uint(b);
-    w[1] = __float_as_uint(l);
-    __builtin_amdgcn_raw_buffer_store_b64(w, mine, kBLOffset + (uint32_t)tid * 8u, 0, kCPolDevice);
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc4(o, i)), mine, t16,
+                                             (uint32_t)i * (16u * kSplitThreads), kCPolDevice);
+    // (b0, l0, b1, l1)
+    u32x4_t w;
+    w[0] = __float_as_uint(b[0]);
+    w[1] = __float_as_uint(l[0]);
+    w[2] = __float_as_uint(b[R - 1]);
+    w[3] = __float_as_uint(l[R - 1]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, mine, kBLOffset + t16, 0, kCPolDevice);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -264,48 +281,42 @@ __device__ __forceinline__ bool split_merge(const ForwardArgs &a, const SplitJob
   __syncthreads();
   if (*ticket != job.w_hi - job.w_lo) return false;
   if (tid == 0) __hip_atomic_store(a.split_cnt + job.cut, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int own = job.slot >> 1;
-  // the largest row shift over the pieces
-  float m = b;
+  // the largest row shifts over the pieces
+  float m[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) m[r] = b[r];
   for (int w = job.w_lo; w <= job.w_hi; ++w) {
-    if (w == own) continue;
-    const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(
-        slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups)), kBLOffset + (uint32_t)tid * 8u, 0,
-        kCPolDevice);
-    m = fmaxf(m, __uint_as_float(blw[0]));
+    const u32x4_t blw = __builtin_amdgcn_raw_buffer_load_b128(
+        slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups)), kBLOffset + t16, 0, kCPolDevice);
+#pragma unroll
+    for (int r = 0; r < R; ++r) m[r] = fmaxf(m[r], __uint_as_float(blw[2 * r]));
   }
-  // sum in share order
-  f32x16_t acc[4];
-  float lacc = 0.f;
+  // sum in share order, every piece (this one too) read back from its
+  // slot, into o
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = f32x16_t{};
+  for (int i = 0; i < 16; ++i) acc4_set(o, i, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+  for (int r = 0; r < R; ++r) l[r] = 0.f;
   for (int w = job.w_lo; w <= job.w_hi; ++w) {
-    if (w == own) {
-      const float sc = __builtin_amdgcn_exp2f(b - m);
+    const __amdgpu_buffer_rsrc_t piece = slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups));
+    const u32x4_t blw = __builtin_amdgcn_raw_buffer_load_b128(piece, kBLOffset + t16, 0, kCPolDevice);
+    float sc[R];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int r = 0; r < R; ++r) {
+      sc[r] = __builtin_amdgcn_exp2f(__uint_as_float(blw[2 * r]) - m[r]);
+      l[r] = fmaf(__uint_as_float(blw[2 * r + 1]), sc[r], l[r]);
+    }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][e] = fmaf(o[db][e], sc, acc[db][e]);
-      lacc = fmaf(l, sc, lacc);
-    } else {
-      const __amdgpu_buffer_rsrc_t other = slot_rsrc(split_slot(w, job.cut, job.U, job.key_tiles, job.groups));
-      const u32x2_t blw = __builtin_amdgcn_raw_buffer_load_b64(other, kBLOffset + (uint32_t)tid * 8u, 0, kCPolDevice);
-      const float sc = __builtin_amdgcn_exp2f(__uint_as_float(blw[0]) - m);
+    for (int i = 0; i < 16; ++i) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(piece, t16, (uint32_t)i * (16u * kSplitThreads), kCPolDevice);
+      f32x4_t y = acc4(o, i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int db = i >> 2, g = i & 3;
-        const u32x4_t x =
-            __builtin_amdgcn_raw_buffer_load_b128(other, (uint32_t)i * (16u * kSplitThreads) + t16, 0, kCPolDevice);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[db][4 * g + e] = fmaf(__uint_as_float(x[e]), sc, acc[db][4 * g + e]);
-      }
-      lacc = fmaf(__uint_as_float(blw[1]), sc, lacc);
+      for (int e = 0; e < 4; ++e) y[e] = fmaf(__uint_as_float(x[e]), sc[i % R], y[e]);
+      acc4_set(o, i, y);
     }
   }
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = acc[db];
-  l = lacc;
-  b = m;
+  for (int r = 0; r < R; ++r) b[r] = m[r];
   return true;
 }
 

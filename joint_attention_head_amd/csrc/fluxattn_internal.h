@@ -81,11 +81,11 @@ struct ForwardArgs {
 
 // Partial result of one piece of a split query block: per thread of the
 // 512-thread workgroup, 64 fp32 O accumulators (16 float4, stored
-// [float4 index][thread]) then the row shift b and normaliser l (float2
-// per thread).  Two slots per workgroup: the first and the last job of its
-// share.
+// [float4 index][thread]) then the row shifts b and normalisers l of the
+// thread's one or two query rows (float4 (b0, l0, b1, l1) per thread).
+// Two slots per workgroup: the first and the last job of its share.
 constexpr int kSplitThreads = 512;
-constexpr int64_t kSplitPieceFloats = (int64_t)kSplitThreads * 64 + (int64_t)kSplitThreads * 2;
+constexpr int64_t kSplitPieceFloats = (int64_t)kSplitThreads * 64 + (int64_t)kSplitThreads * 4;
 
 // Split workspace: one int32 arrival count per tail block, in a region
 // sized for the largest setting (2 * kMaxGroups counts, so that the slots

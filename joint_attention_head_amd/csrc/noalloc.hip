@@ -15,7 +15,7 @@ namespace {
 
 // Room for a split over 256 workgroups, one per compute unit of an MI355X
 // (the default setting's launch there): 128 KiB of arrival counts and two
-// 132 KiB partial slots per workgroup, 66.1 MiB.  Every GPU the library runs
+// 136 KiB partial slots per workgroup, 68.1 MiB.  Every GPU the library runs
 // this entry point on holds its own copy until the process ends.
 constexpr int32_t kScratchGroups = 256;
 constexpr uint64_t kScratchBytes = split_workspace_bytes_for(kScratchGroups);

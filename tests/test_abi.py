@@ -100,10 +100,10 @@ def fused8(lib, q=Q, k=K, v=V, sq=SQ, sk=SK, sv=SV, o=O, wq=WQ, pos=POS, b=B, h=
 
 
 # Split workspace layout: 2 * 16384 int32 arrival counts, then two partial
-# slots per workgroup of 512 threads x (64 fp32 accumulators + shift and
-# normaliser).
+# slots per workgroup of 512 threads x (64 fp32 accumulators + shifts and
+# normalisers of the thread's one or two query rows, a float4).
 COUNT_BYTES = 2 * 16384 * 4
-SLOT_BYTES = 512 * (64 + 2) * 4
+SLOT_BYTES = 512 * (64 + 4) * 4
 
 
 def ws_bytes(lib, b, h, n, groups, d=D):

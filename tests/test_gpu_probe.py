@@ -1,6 +1,7 @@
 """The matrix-core probe (include/fluxattn_probe.h) on the GPU: it runs, its
-flop count is 2*32*32*k per MFMA times 8 MFMAs per round per wave, and every
-wave leaves a finite sum in the sink."""
+flop count per round and wave is that of 8 MFMAs of 32x32xk (the 16x16x32
+kind: 16 MFMAs, the same flops), and every wave leaves a finite sum in the
+sink."""
 import pytest
 import torch
 
@@ -9,7 +10,7 @@ import joint_attention_head_amd as fa
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind,k", [("bf16", 16), ("fp8", 64)])
+@pytest.mark.parametrize("kind,k", [("bf16", 16), ("fp8", 64), ("bf16_16x16x32", 16)])
 def test_probe_runs_and_counts_flops(kind, k):
     wg = 16
     sink = torch.full((wg * 8,), float("nan"), dtype=torch.float32, device="cuda")
