@@ -445,6 +445,32 @@ def test_joint_bf16_parity_t2i_2048_sampled():
     assert torch.all(ones == 1.0)
 
 
+# Ragged edges at every boundary of the bf16 kernel's lane layout: a lane
+# holds keys 16 kb + 4 g + r of each 64-key tile and the two query rows
+# l % 16 and 16 + l % 16 of its wave's 32, so a last key tile ending at
+# N mod 64 in {4, 15, 16, 17, 32, 48, 63} and a last query block ending at
+# N mod 256 in {4, 15, 16, 17, 32, 48, 63, 240} cut those groups at
+# different places (text tokens + an 8 x 8 image grid).  The fused form is
+# held to the unrounded chain (RMSNorm + RoPE of the queries in fp64).
+EDGE_N = (260, 272, 273, 288, 304, 319, 496, 783)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_forward_bf16_ragged_lane_edges(fused):
+    for i, N in enumerate(EDGE_N):
+        inp = small(1, 2, N - 64, (8, 8), seed=10 + i)
+        assert inp.q.shape[2] == N
+        if fused:
+            o = fa.fluxattn_forward_fused_bf16(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.w_q), dev(inp.pos))
+            ref = oracle.attention(_q_prime(f64(inp.q), inp.w_q, inp.pos), f64(inp.k), f64(inp.v))
+        else:
+            o = run_forward_bf16(inp)
+            ref = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v))
+        torch.cuda.synchronize()
+        rel = check_close(f64(o), ref, BF16_TOL, f"forward bf16 {'fused ' if fused else ''}N={N}")
+        assert rel < 1e-2
+
+
 FUSED_CASES = {
     "tiny": lambda: inputs("tiny"),
     "flux_dev_512": lambda: inputs("flux_dev_512"),
