@@ -227,12 +227,12 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   const float c = a.scale_log2;
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t *)lds);
 
-  // ---- lane constants (bytes).  Each group loads half of every tile:
-  // keys [32 g, 32 g + 32).
-  //  K by direct copies: wave gw of group g copies rows
-  //     32 g + 8 gw .. +8 with two buffer_load_dwordx4 ... lds; lane l of
-  //     copy i fetches the chunk the K swizzle puts at LDS slot row
-  //     32 g + 8 gw + 4 i + l / 16, chunk position l % 16.
+  // ---- lane constants (bytes).  Each ping-pong group loads half of every
+  // tile: keys [32 group, 32 group + 32).
+  //  K by direct copies: wave gw of the group copies rows
+  //     32 group + 8 gw .. +8 with two buffer_load_dwordx4 ... lds; lane l
+  //     of copy i fetches the chunk the K swizzle puts at LDS slot row
+  //     32 group + 8 gw + 4 i + l / 16, chunk position l % 16.
   uint32_t k_dgoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
