@@ -30,6 +30,12 @@ on a bounded sample of the main workload under "cpu_baseline".  Each roofline
 also carries the MFMA-busy fraction and sustained clock of its kernel from
 the committed rocprofv3 counter summary ("counters", null once the kernel
 source has changed since it was taken).
+
+The main workload is timed after exactly --warmup untimed steps.  The others
+warm up for at least --min-warmup-s seconds of their own steps (default
+0.25 s): after an idle pause, such as generating a workload's inputs on the
+host, the chip's clocks ramp for some tens of milliseconds, longer than a few
+steps of a small workload.
 """
 from __future__ import annotations
 
@@ -139,6 +145,11 @@ def parse():
                         "> 0 = that many workgroups")
     p.add_argument("--no-mfma-ceiling", dest="mfma_ceiling", action="store_false",
                    help="skip the matrix-core ceiling (MFMA-only probe kernel, bf16 and fp8)")
+    p.add_argument("--min-warmup-s", type=float, default=0.25,
+                   help="the secondary workloads (--also, --fp8, the per-workload table, the extras) warm up "
+                        "for at least this many seconds of their own steps: after an idle pause (input "
+                        "generation on the host) the chip's clocks ramp for some tens of milliseconds, "
+                        "longer than a few steps of a small workload")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB elementwise copy (HBM counter calibration)")
     return p.parse_args()
@@ -228,7 +239,10 @@ def clock_sampler():
 
 
 def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int = 0, clock: bool = False,
-            inputs=None):
+            inputs=None, min_warmup_s: float = 0.0):
+    """Time `steps` steps of workload `name` after `warmup` untimed ones; with
+    min_warmup_s > 0 the warmup goes on, four steps at a time, until that
+    many seconds of this workload's steps have run."""
     import torch
 
     import joint_attention_head_amd as fa
@@ -280,9 +294,16 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
         if ev is not None:
             ev[2].record(stream)
 
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    warm_steps = warmup
+    while time.perf_counter() - t_warm < min_warmup_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        warm_steps += 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -333,6 +354,7 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
         "flops": flops,
         "split_workspace_bytes": ws.nbytes if ws is not None else 0,
         "sustained": sustained,
+        "warmup_steps": warm_steps,
     }
     del q, k, v, qn, kn, o, ws
     if fp8:
@@ -470,7 +492,7 @@ def main():
           f"{main_res['sustained']}", file=sys.stderr, flush=True)
     also = None
     if args.also:
-        r = run_gpu(args.also, args.steps, args.warmup, args.path, args.groups)
+        r = run_gpu(args.also, args.steps, args.warmup, args.path, args.groups, min_warmup_s=args.min_warmup_s)
         done[args.also] = r
         w = r["workload"]
         also = {
@@ -483,11 +505,13 @@ def main():
             "forward_ms_min": round(r["forward_ms_min"], 4),
             "prologue_gbs": round(r["prologue_gbs"], 1),
             "prologue_gbs_mall_flushed": round(r["prologue_gbs_mall_flushed"], 1),
+            "warmup_steps": r["warmup_steps"],
         }
         print(f"bench: {args.also} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
     fp8 = None
     if args.fp8:
-        r = run_gpu(args.fp8, args.steps, args.warmup, args.path, args.groups, args.clock)
+        r = run_gpu(args.fp8, args.steps, args.warmup, args.path, args.groups, args.clock,
+                    min_warmup_s=args.min_warmup_s)
         done[args.fp8] = r
         w = r["workload"]
         fp8 = {
@@ -511,6 +535,7 @@ def main():
                 "launch_us_median": round(r["prologue_us_median"], 2),
             },
             "split_workspace_bytes": r["split_workspace_bytes"],
+            "warmup_steps": r["warmup_steps"],
         }
         print(f"bench: {args.fp8} fp8 forward {r['forward_ms']:.4f} ms; sustained {r['sustained']}",
               file=sys.stderr, flush=True)
@@ -523,7 +548,8 @@ def main():
         for name in WORKLOADS:
             r = done.get(name)
             if r is None:
-                r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups)
+                r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups,
+                            min_warmup_s=args.min_warmup_s)
             w = r["workload"]
             peak = FP8_PEAK_TFLOPS if w.dtype == "fp8" else BF16_PEAK_TFLOPS
             all_configs[name] = {
@@ -537,6 +563,7 @@ def main():
                 "prologue_gbs": round(r["prologue_gbs"], 1),
                 "prologue_gbs_mall_flushed": round(r["prologue_gbs_mall_flushed"], 1),
                 "split_workspace_bytes": r["split_workspace_bytes"],
+                "warmup_steps": r["warmup_steps"],
             }
             print(f"bench: {name} forward {r['forward_ms']:.4f} ms", file=sys.stderr, flush=True)
     extras = None
@@ -552,7 +579,8 @@ def main():
         }
         extras = {}
         for name, inp in cases.items():
-            r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups, inputs=inp)
+            r = run_gpu(name, max(args.steps, 10), max(args.warmup, 3), args.path, args.groups, inputs=inp,
+                        min_warmup_s=args.min_warmup_s)
             w = r["workload"]
             extras[name] = {"B": w.B, "H": w.H, "N": w.N, "dtype": w.dtype,
                             "forward_ms_median": round(r["forward_ms_median"], 4),
