@@ -104,9 +104,10 @@ typedef struct {
 /*
  * Key-range split of one attention launch (an execution choice: the function
  * computed is the one each entry point describes).  A launch normally runs
- * one workgroup per 256-query block of each (b,h), in rounds of one
- * workgroup per compute unit, and its last round can leave compute units
- * idle.  A split launch instead runs G persistent workgroups: all but the
+ * at most one persistent workgroup per compute unit, each computing whole
+ * 256-query blocks of each (b,h) in turn, in rounds of one block per
+ * compute unit, and its last round can leave compute units idle.  A split
+ * launch instead runs G persistent workgroups: all but the
  * last one or two rounds of blocks go whole, in launch order, and the
  * remaining blocks' (query block, 64-key tile) pairs, in (b, h, query
  * block, key tile) order, are dealt out as G equal contiguous shares.  A

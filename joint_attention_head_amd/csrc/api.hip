@@ -394,11 +394,11 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
   const fluxattn_status dev = device_ok();
   if (dev != FLUXATTN_OK) return dev;
 
-  // the split plan depends on the device's compute units, so the workspace
-  // is checked after the device
+  // the split plan and the uncut launch's grid depend on the device's
+  // compute units, so the workspace is checked after the device
   const int32_t setting = split_setting(split);
   int32_t cus = 0;
-  if (setting == 0) {
+  {
     int d = 0;
     if (hipGetDevice(&d) != hipSuccess) {
       (void)hipGetLastError();
@@ -406,7 +406,8 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
     }
     cus = compute_units(d);
   }
-  const SplitPlan plan = split_plan_for(forward_grid_blocks(BH, N), forward_key_tiles(N), setting, cus);
+  const int64_t nb = forward_grid_blocks(BH, N);
+  const SplitPlan plan = split_plan_for(nb, forward_key_tiles(N), setting, cus);
   const int64_t groups = plan.groups;
   if (need_out) {
     // validation only: report the workspace the launch needs
@@ -467,6 +468,8 @@ fluxattn_status forward_prepare(View q, View k, View v, const float *q_scale, co
     a.split_groups = static_cast<int32_t>(groups);
     a.split_whole = static_cast<int32_t>(plan.whole);
   }
+  // uncut: one persistent workgroup per compute unit (or per block)
+  a.whole_groups = static_cast<int32_t>(cus > 0 ? std::min<int64_t>(nb, cus) : nb);
   strided = !(is_contiguous(q, H, N, D) && is_contiguous(k, H, N, D) && is_contiguous(v, H, N, D) &&
               is_contiguous(o, H, N, D));
   return FLUXATTN_OK;

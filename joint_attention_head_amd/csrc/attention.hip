@@ -55,11 +55,14 @@
 //  * blockIdx is remapped so that the workgroups the dispatcher sends to one
 //    XCD (blockIdx % 8) take consecutive query tiles of the same (b,h) and
 //    share its K/V stream through that XCD's L2.
-//  * A workgroup runs a list of jobs (attn_common.h): normally one whole
-//    query block; when the host balances the last round, a persistent grid
-//    takes whole blocks in launch order and then an equal share of the
-//    tail's (query block, key tile) pairs, a cut block's pieces being
-//    merged by whichever finishes last.
+//  * A workgroup runs a list of jobs (attn_common.h): the launch is a
+//    persistent grid of at most one workgroup per compute unit.  Uncut,
+//    each takes whole blocks of its XCD's range in turn; when the host
+//    balances the last round, it takes whole blocks in launch order and then
+//    an equal share of the tail's (query block, key tile) pairs, a cut
+//    block's pieces being merged by whichever finishes last.
+//  * A job requests its queries, then its first three tiles' copies, and
+//    normalises and rotates the queries (fused form) while the tiles arrive.
 // FP8 inputs run on the fp8 matrix cores instead (attention_fp8.hip).
 #include "attn_common.h"
 
@@ -136,8 +139,17 @@ __device__ __forceinline__ float quad_sum(float x) {
 // (q_row[h], h = 0, 1) and of each the dims 32 ks + 8 g .. +8 (ks = 0..3):
 // the other 96 dims of a query are in lanes lane ^ 16, ^ 32, ^ 48.  The one
 // bf16 rounding of Q' is the same as the prologue's, applied to c Q'.
-__device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[2][4], const ForwardArgs &a, const RopeLds *rope,
-                                             const HeadView &vq, const int (&q_row)[2], int g) {
+// In two parts, so that the job's first tile copies go out between them:
+// load_q_issue requests the raw queries and position ids (no wait) and
+// reads the rows' norm weights from the LDS table; q_transform does the
+// arithmetic.
+struct QueryIn {
+  int pos[2][3];        // position ids of the lane's two queries
+  float4 w[2][4][2];    // their norm weights, dims 32 ks + 8 g .. +8
+};
+__device__ __forceinline__ void load_q_issue(bf16x8_t (&qf)[2][4], QueryIn &in, const ForwardArgs &a,
+                                             const RopeLds *tab, const HeadView &vq, const int (&q_row)[2],
+                                             int g) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -146,6 +158,23 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[2][4], const Forward
       const uint32_t off = (uint32_t)q_row[h] * vq.row + (uint32_t)((32 * ks + 8 * g) * 2);
       qf[h][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // rows past N belong to no token: any valid row serves, their outputs
+    // are never stored
+    const int tok = min(q_row[h], a.N - 1);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) in.pos[h][i] = a.pos[3 * tok + i];
+    const float *w_q = tab->wq[stream_of(a, tok)];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      in.w[h][ks][0] = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g);
+      in.w[h][ks][1] = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g + 4);
+    }
+  }
+}
+__device__ __forceinline__ void q_transform(bf16x8_t (&qf)[2][4], const QueryIn &in, const ForwardArgs &a,
+                                            const RopeLds *tab, int g) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float ss = 0.f;
@@ -160,21 +189,16 @@ __device__ __forceinline__ void load_q_fused(bf16x8_t (&qf)[2][4], const Forward
     // rstd and the logit scale c folded into the weights: Q' c = (x w rstd c)
     // rotated
     const float rs = a.scale_log2 / sqrtf(ss * (1.0f / kHeadDim) + a.eps);
-    // position ids of this query (rows past N belong to no token: any valid
-    // row serves, their outputs are never stored)
-    const int tok = min(q_row[h], a.N - 1);
-    const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
-    const float *w_q = stream_weights(a, tok);
+    const float pf[3] = {(float)in.pos[h][0], (float)in.pos[h][1], (float)in.pos[h][2]};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = (float)qf[h][ks][i];
-      const float4 w0 = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g);
-      const float4 w1 = *reinterpret_cast<const float4 *>(w_q + 32 * ks + 8 * g + 4);
+      const float4 w0 = in.w[h][ks][0], w1 = in.w[h][ks][1];
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       float sn[4], cs[4];
-      rotations4(rope, pf, 16 * ks + 4 * g, sn, cs);   // pairs 16 ks + 4 g + m
+      rotations4(tab, pf, 16 * ks + 4 * g, sn, cs);   // pairs 16 ks + 4 g + m
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float u = x[2 * m] * (w[2 * m] * rs);
@@ -203,12 +227,13 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
   // ---- per-head base pointers, token-row pitches and buffer extents
   const HeadView vq = head_view<STRIDED>(a.q, a.sq, 2, bh, a.H, N);
   // ---- queries: qf[h][ks] = Q[q_row[h]][32 ks + 8 g .. +8), the B
-  // operands of QK^T (first, so the fused transform's temporaries overlap
-  // no other state)
+  // operands of QK^T, requested first (the fused transform follows the
+  // first tile copies below)
   const int q_row[2] = {qt * kBR + wave * 32 + l16, qt * kBR + wave * 32 + 16 + l16};
   bf16x8_t qf[2][4];
+  QueryIn qin;
   if constexpr (FUSEQ) {
-    load_q_fused(qf, a, rope, vq, q_row, g);
+    load_q_issue(qf, qin, a, rope, vq, q_row, g);
   } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
@@ -293,14 +318,48 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
         : "memory", "scc");
   };
 
-  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
-  for (int j = 0; j < 3 && j < T; ++j) {
-    const i32x4_t w = tile_words(vk, kt0 + j, kBC);
-    k_dma_one(w, j * kKTileBytes, 0);
-    k_dma_one(w, j * kKTileBytes, 1);
-    const i32x4_t wv = tile_words(vv, kt0 + j, kBC);
-    v_dma_one(wv, j * kKTileBytes, 0);
-    v_dma_one(wv, j * kKTileBytes, 1);
+  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS, by the same
+  // copies as in the loop but through the builtin, so that the compiler
+  // counts them: the query transform then waits for the queries only and
+  // runs while the tiles arrive.  Tile indices are clamped to T - 1 (a fixed
+  // count of copies; extra ones land in slots no step reads).
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    typedef __attribute__((address_space(3))) void *lds_void_t;
+    lds_char_t *dst = (lds_char_t *)lds + 256 * (32 * group + 8 * gw);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t tile = (uint32_t)(kt0 + min(j, T - 1)) * (uint32_t)kBC;   // first key
+      const uint32_t skip_k = tile * vk.row, skip_v = tile * vv.row;   // the views' row pitches may differ
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(vk.base + skip_k, vk.bytes - skip_k);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vv.base + skip_v, vv.bytes - skip_v);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t)(dst + j * kKTileBytes + 1024 * i), 16,
+                                                 k_dgoff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t)(dst + kVRingOffset + j * kKTileBytes + 1024 * i),
+                                                 16, v_dgoff[i], 0, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FUSEQ) {
+    // the transform's inputs and outputs pass through empty asm statements
+    // after the copies and before their wait, which pins the transform
+    // between the two (otherwise the compiler moves parts of it to either
+    // side)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[h][ks]));
+#pragma unroll
+      for (int i = 0; i < 3; ++i) asm volatile("" : "+v"(qin.pos[h][i]));
+    }
+    q_transform(qf, qin, a, rope, g);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[h][ks]));
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -561,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   __shared__ RopeLds rope;
 
   const int tid = threadIdx.x;
-  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid);   // before the barrier in pingpong_order
+  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid, kThreads);   // before the barrier in pingpong_order
   // ---- ping-pong groups: the two waves of a SIMD land in different groups
   const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
   const int group = order & 1;
@@ -573,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
   __shared__ SplitRange range_lds[kWaves];
   SplitRange *rs = &range_lds[tid >> 6];
   {
-    const SplitRange r = split_range(a, kBR, kBC, xcd_logical_block(blockIdx.x, gridDim.x));
+    const SplitRange r = split_range(a, kBR, kBC, blockIdx.x, gridDim.x);
     if ((tid & 63) == 0) *rs = r;
   }
   for (;;) {
@@ -588,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(ForwardArgs a) {
 template <bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
   const int64_t ntiles = (a.N + kBR - 1) / kBR;
-  const int64_t grid = a.split_groups > 0 ? a.split_groups : ntiles * a.BH;
+  const int64_t grid = a.split_groups > 0 ? a.split_groups : std::min<int64_t>(a.whole_groups, ntiles * a.BH);
   // Raise the dynamic-LDS limit once per device (idempotent, so a race
   // between threads only repeats the call).
   static std::atomic<uint64_t> attr_done{0};

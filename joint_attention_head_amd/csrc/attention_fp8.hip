@@ -126,16 +126,38 @@ __device__ __forceinline__ f32x16_t mfma_f8_bscaled(i32x8_t a, i32x8_t b, f32x16
 // logits c*S directly, and the largest code of the query lies in (224, 448].
 // Returns the E8M0 scale 127 + e in `sb`.  The lane holds dims
 // 64 kk + 32 hi + (0..31); the other 64 are in lane ^ 32.
-__device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const ForwardArgs &a, const RopeLds *rope,
-                                             const HeadView &vq,
-                                             int q_row, int hi, float in_scale, float g) {
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
+// In two parts, so that the job's first tile copies go out between them:
+// load_q_issue requests the raw codes and the position ids (no wait) and
+// reads the row's norm weights from the LDS table; q_transform does the
+// arithmetic.
+struct QueryIn {
   u32x4_t raw[4];   // raw[2 kk + t]: dims 64 kk + 32 hi + 16 t + (0..15)
+  int pos[3];       // position ids of the lane's query
+  float4 w[16];     // w[4 c + q]: norm weights of dims 64 (c / 2) + 32 hi + 16 (c % 2) + 4 q .. +4
+};
+__device__ __forceinline__ void load_q_issue(QueryIn &in, const ForwardArgs &a, const RopeLds *tab,
+                                             const HeadView &vq, int q_row, int hi) {
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    raw[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rq, (uint32_t)q_row * vq.row + (uint32_t)(64 * (c >> 1) + 32 * hi + 16 * (c & 1)),
-                                             0, 0));
+    in.raw[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rq, (uint32_t)q_row * vq.row + (uint32_t)(64 * (c >> 1) + 32 * hi + 16 * (c & 1)),
+                                                0, 0));
+  // rows past N belong to no token: any valid row serves, their outputs are
+  // never stored
+  const int tok = min(q_row, a.N - 1);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) in.pos[i] = a.pos[3 * tok + i];
+  const float *w_q = tab->wq[stream_of(a, tok)];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      in.w[4 * c + q4] = *reinterpret_cast<const float4 *>(w_q + 64 * (c >> 1) + 32 * hi + 16 * (c & 1) + 4 * q4);
+}
+__device__ __forceinline__ void q_transform(i32x8_t (&qf)[2], int &sb, const QueryIn &in, const ForwardArgs &a,
+                                            const RopeLds *tab, int hi, float in_scale, float g) {
+  const u32x4_t(&raw)[4] = in.raw;
   // E4M3 codes as float; the dequantisation scale s_q is folded into the
   // normalisation: x_deq w rstd = x w (s_q rstd), with rstd from s_q^2 sum x^2
   float x[64];
@@ -158,24 +180,19 @@ __device__ __forceinline__ void load_q_fused(i32x8_t (&qf)[2], int &sb, const Fo
     ss = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // all 128 dims of this query
   }
   const float rs = in_scale / sqrtf(ss * (in_scale * in_scale) * (1.0f / kHeadDim) + a.eps);
-  // rows past N belong to no token: any valid row serves, their outputs are
-  // never stored
-  const int tok = min(q_row, a.N - 1);
-  const float pf[3] = {(float)a.pos[3 * tok + 0], (float)a.pos[3 * tok + 1], (float)a.pos[3 * tok + 2]};
-  const float *w_q = stream_weights(a, tok);
+  const float pf[3] = {(float)in.pos[0], (float)in.pos[1], (float)in.pos[2]};
   float amax = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int d0 = 64 * (c >> 1) + 32 * hi + 16 * (c & 1);   // first dim of this chunk
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       // pairs d0 / 2 + 4 g + (0..3)
       float sn[4], cs[4];
-      rotations4(rope, pf, 32 * (c >> 1) + 16 * hi + 8 * (c & 1) + 4 * g, sn, cs);
+      rotations4(tab, pf, 32 * (c >> 1) + 16 * hi + 8 * (c & 1) + 4 * g, sn, cs);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const int q4 = 2 * g + qq;
-        const float4 w = *reinterpret_cast<const float4 *>(w_q + d0 + 4 * q4);
+        const float4 w = in.w[4 * c + q4];
         const float wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -292,21 +309,19 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
         : "memory", "scc");
   };
 
-  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS
-  for (int j = 0; j < 3 && j < T; ++j) {
-    k_dma(tile_words(vk, kt0 + j, kBC), j * kKTileBytes);
-    v_dma(tile_words(vv, kt0 + j, kBC), j * kVTileBytes);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
   // ---- queries: qf[kk] = codes of dims 64 kk + 32 hi .. +32 of this
-  // lane's query; c = softmax scale * log2 e * (q scale) * (k scale)
+  // lane's query; c = softmax scale * log2 e * (q scale) * (k scale).
+  // Requested first; the fused transform follows the first tile copies.
   const int q_row = qt * kBR + wave * 32 + l32;
+  // the head's dequantisation scales, read before the tile copies go out
+  // (a later read would wait for them)
+  const float q_scale = a.q_scale[bh], k_scale = a.k_scale[bh], v_scale = a.v_scale[bh];
   i32x8_t qf[2];
   float qs = 1.f;
   int qsb = 127;   // fused: E8M0 B scale of the QK^T MFMAs, c folded in
+  QueryIn qin;
   if constexpr (FUSEQ) {
-    load_q_fused(qf, qsb, a, rope, vq, q_row, hi, a.q_scale[bh], a.scale_log2 * a.k_scale[bh]);
+    load_q_issue(qin, a, rope, vq, q_row, hi);
   } else {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(vq.base, vq.bytes);
 #pragma unroll
@@ -316,12 +331,48 @@ __device__ __forceinline__ void attn_job(const ForwardArgs &a, char *lds, const 
       const i32x4_t y = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
       qf[kk] = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    qs = a.q_scale[bh];
+    qs = q_scale;
   }
+
+  // ---- rings, before the loop: K and V tiles 0, 1, 2 in LDS, by the same
+  // copies as in the loop but through the builtin, so that the compiler
+  // counts them: the query transform then waits for the queries only and
+  // runs while the tiles arrive.  Tile indices are clamped to T - 1 (a fixed
+  // count of copies; extra ones land in slots no step reads).
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    typedef __attribute__((address_space(3))) void *lds_void_t;
+    lds_char_t *dst = (lds_char_t *)lds + 128 * (32 * group + 8 * gw);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t tile = (uint32_t)(kt0 + min(j, T - 1)) * (uint32_t)kBC;   // first key
+      const uint32_t skip_k = tile * vk.row, skip_v = tile * vv.row;   // the views' row pitches may differ
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vk.base + skip_k, vk.bytes - skip_k),
+                                               (lds_void_t)(dst + j * kKTileBytes), 16, k_dgoff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vv.base + skip_v, vv.bytes - skip_v),
+                                               (lds_void_t)(dst + kVRingOffset + j * kVTileBytes), 16, v_dgoff, 0,
+                                               0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FUSEQ) {
+    // the transform's inputs and outputs pass through empty asm statements
+    // after the copies and before their wait, which pins the transform
+    // between the two
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qin.raw[c]));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) asm volatile("" : "+v"(qin.pos[i]));
+    q_transform(qf, qsb, qin, a, rope, hi, q_scale, a.scale_log2 * k_scale);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) asm volatile("" : "+v"(qf[kk]));
+    asm volatile("" : "+v"(qsb));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // unfused: x = c*S - b by one FMA per score; fused: the MFMA's B scale
   // applies c and its accumulator starts at -b (`bias`)
-  const float c = a.scale_log2 * qs * a.k_scale[bh];
-  const float o_scale = a.v_scale[bh];
+  const float c = a.scale_log2 * qs * k_scale;
+  const float o_scale = v_scale;
 
   f32x16_t o[4];
 #pragma unroll
@@ -560,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   __shared__ RopeLds rope;
 
   const int tid = threadIdx.x;
-  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid);   // before the barrier in pingpong_order
+  if constexpr (FUSEQ) rope_lds_fill(&rope, a, tid, kThreads);   // before the barrier in pingpong_order
   const int order = pingpong_order(simd_of_wave, tid >> 6, tid & 63);
   const int group = order & 1;
   const int gw = order >> 1;                   // wave index inside the group
@@ -571,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
   __shared__ SplitRange range_lds[kWaves];
   SplitRange *rs = &range_lds[tid >> 6];
   {
-    const SplitRange r = split_range(a, kBR, kBC, xcd_logical_block(blockIdx.x, gridDim.x));
+    const SplitRange r = split_range(a, kBR, kBC, blockIdx.x, gridDim.x);
     if ((tid & 63) == 0) *rs = r;
   }
   for (;;) {
@@ -585,7 +636,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(ForwardArgs a) {
 
 template <bool FUSEQ, bool STRIDED>
 hipError_t launch(const ForwardArgs &a, hipStream_t s) {
-  const int64_t grid = a.split_groups > 0 ? a.split_groups : (int64_t)((a.N + kBR - 1) / kBR) * a.BH;
+  const int64_t grid =
+      a.split_groups > 0 ? a.split_groups : std::min<int64_t>(a.whole_groups, (int64_t)((a.N + kBR - 1) / kBR) * a.BH);
   // Raise the dynamic-LDS limit once per device (idempotent, so a race
   // between threads only repeats the call).
   static std::atomic<uint64_t> attr_done{0};

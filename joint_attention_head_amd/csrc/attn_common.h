@@ -88,8 +88,10 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int total) {
   return xcd * q8 + min(xcd, r8) + (bid >> 3);
 }
 
-// ---- Key-range split.  Without a split, workgroup w computes query block
-// w whole (blocks in (b*h, query tile) order).  With split_groups = G
+// ---- Key-range split.  Without a split, the launch has whole_groups
+// persistent workgroups, the same number on every XCD but for the last
+// partial row of eight; the workgroups of XCD x take its contiguous range of
+// blocks (as xcd_logical_block deals them), in turn.  With split_groups = G
 // persistent workgroups and nb blocks, the first F = split_whole rounds
 // (chosen on the host, F G < nb) go as whole blocks in launch order:
 // workgroup w takes blocks w, w + G, ..., so the workgroups running at one
@@ -123,10 +125,11 @@ struct SplitJob {
   int groups;
 };
 
-__device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows, int keys, int logical) {
+__device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows, int keys, int bid, int grid) {
   SplitRange r;
   r.q_tiles = (a.N + rows - 1) / rows;
   r.key_tiles = (a.N + keys - 1) / keys;
+  const int logical = xcd_logical_block(bid, grid);
   r.logical = logical;
   r.blk = logical;
   r.groups = a.split_groups;
@@ -141,8 +144,15 @@ __device__ __forceinline__ SplitRange split_range(const ForwardArgs &a, int rows
     r.u = r.start;
     r.end = r.U * (logical + 1) / G;
   } else {
-    r.whole = 1;
-    r.stride = 0;
+    // XCD x holds blocks [x q8 + min(x, r8), + q8 + (x < r8)) and the
+    // workgroups bid = x, x + 8, ... of the grid; its j-th takes the range's
+    // blocks j, j + slots, ...
+    const int nb = a.BH * r.q_tiles;
+    const int x = bid & 7, j = bid >> 3, q8 = nb >> 3, r8 = nb & 7;
+    const int count = q8 + (x < r8), slots = (grid + 7 - x) >> 3;
+    r.blk = x * q8 + min(x, r8) + j;
+    r.stride = slots;
+    r.whole = j < count ? (count - j + slots - 1) / slots : 0;
     r.base = 0;
     r.U = r.start = r.u = r.end = 0;
   }
@@ -354,24 +364,33 @@ __device__ __forceinline__ i32x4_t tile_words(const HeadView &v, int t, int tile
   return rsrc_words(v.base + skip, v.bytes - skip);
 }
 
-// Norm weights of a token's stream.
-__device__ __forceinline__ const float *stream_weights(const ForwardArgs &a, int tok) {
-  const int sid = (tok >= a.streams.start[1]) + (tok >= a.streams.start[2]) + (tok >= a.streams.start[3]);
-  return a.w_q + sid * kHeadDim;
-}
-
-// Rotation rates of the fused query prologue in LDS: rate[a][p] as in the
-// arguments (one nonzero axis per pair).  Filled by threads 0..63 before
-// the workgroup's first barrier.
+// Tables of the fused query prologue in LDS: the rotation rates rate[a][p]
+// as in the arguments (one nonzero axis per pair), and the query norm
+// weights of each stream.  Filled by the workgroup's threads before its
+// first barrier.
 struct alignas(16) RopeLds {
   float rate[3][kPairs];
+  float wq[4][kHeadDim];
 };
 
-__device__ __forceinline__ void rope_lds_fill(RopeLds *t, const ForwardArgs &a, int tid) {
+// Streams of the launch: those whose first token lies inside the sequence
+// (the host sets the starts of absent ones past N).
+__device__ __forceinline__ int stream_count(const ForwardArgs &a) {
+  return 1 + (a.streams.start[1] <= a.N) + (a.streams.start[2] <= a.N) + (a.streams.start[3] <= a.N);
+}
+
+// Stream of a token.
+__device__ __forceinline__ int stream_of(const ForwardArgs &a, int tok) {
+  return (tok >= a.streams.start[1]) + (tok >= a.streams.start[2]) + (tok >= a.streams.start[3]);
+}
+
+__device__ __forceinline__ void rope_lds_fill(RopeLds *t, const ForwardArgs &a, int tid, int threads) {
   if (tid < kPairs) {
 #pragma unroll
     for (int ax = 0; ax < 3; ++ax) t->rate[ax][tid] = a.rope_rate[ax][tid];
   }
+  const int n = stream_count(a) * kHeadDim;
+  for (int i = tid; i < n; i += threads) t->wq[i / kHeadDim][i % kHeadDim] = a.w_q[i];
 }
 
 // (sin, cos) of the rotations of pairs p0 .. p0+3 (p0 a multiple of 4) of a

@@ -77,6 +77,10 @@ struct ForwardArgs {
   int32_t *split_cnt;
   int32_t split_groups;
   int32_t split_whole;      // rounds of whole blocks before the tail
+  // Uncut launches (split_groups <= 0): a persistent grid of this many
+  // workgroups (at most one per compute unit and per query block), each
+  // taking whole blocks in turn.
+  int32_t whole_groups;
 };
 
 // Partial result of one piece of a split query block: per thread of the
