@@ -117,9 +117,11 @@ typedef struct {
  * Results differ from the uncut launch by the P roundings (each piece's P
  * is relative to its own running shift) and fp32 summation order, and are
  * deterministic.
- *   groups     0: G = the device's compute units; the launch is cut only
- *                 with at least two rounds of blocks, when whole blocks
- *                 would leave more than 3% of the last round idle;
+ *   groups     0: G = the device's compute units; the launch is cut with
+ *                 at least two rounds of blocks when whole blocks would
+ *                 leave more than 3% of the last round idle, and between
+ *                 one and two rounds when the second round would be less
+ *                 than 7/12 full (one whole round, then the rest cut);
  *              > 0 (at most 16384): G = groups, at most one per key tile of
  *                 the cut blocks; always cut (with more workgroups than
  *                 blocks, blocks are cut into several pieces);

@@ -184,20 +184,29 @@ SplitPlan split_plan_for(int64_t nb, int64_t key_tiles, int32_t setting, int32_t
   int64_t groups = setting > 0 ? setting : cus;
   if (groups < 2) return p;
   if (setting == 0) {
-    // fewer than two rounds: measured slower cut than whole (at one to two
-    // rounds the shares stream keys out of step; with fewer blocks than
-    // compute units the per-job start-up and the merges outweigh the idle
-    // units: N = 1536 runs 19% (bf16) and 26% (fp8) slower cut)
-    if (nb < 2 * groups) return p;
-    // whole rounds, then a tail: cut when whole blocks would leave more
-    // than 3% of the last round idle
-    const int64_t rounds = (nb + groups - 1) / groups;
-    if (nb * 100 >= rounds * groups * 97) return p;
+    // at most one round: never cut (the per-job start-up and the merges
+    // outweigh the idle units: N = 1536 runs 19% (bf16) and 26% (fp8)
+    // slower cut)
+    if (nb <= groups) return p;
+    if (nb < 2 * groups) {
+      // one to two rounds: one whole round, then the rest cut, when the
+      // second round would be less than 7/12 full (its shares stream keys
+      // out of step, and a part-empty round runs at a higher clock; at
+      // N = 4608 cutting measured +18% at 27% full, +2.5% at 55%, -1.2% at
+      // 62% and -2.6% at 69%)
+      if ((nb - groups) * 12 >= groups * 7) return p;
+    } else {
+      // whole rounds, then a tail: cut when whole blocks would leave more
+      // than 3% of the last round idle
+      const int64_t rounds = (nb + groups - 1) / groups;
+      if (nb * 100 >= rounds * groups * 97) return p;
+    }
   }
-  // all but the last one or two rounds whole; every share holds at least
-  // one pair of the tail (the merge reads a slot of every share between a
-  // block's first and last)
-  const int64_t whole = nb >= 2 * groups ? nb / groups - 1 : 0;
+  // all but the last one or two rounds whole (the default setting keeps
+  // one whole round between one and two rounds); every share holds at
+  // least one pair of the tail (the merge reads a slot of every share
+  // between a block's first and last)
+  const int64_t whole = nb >= 2 * groups ? nb / groups - 1 : (setting == 0 ? 1 : 0);
   const int64_t tail = nb - whole * groups;
   groups = std::min<int64_t>(groups, tail * key_tiles);
   if (groups < 2 || (setting == 0 && nb == groups)) return p;

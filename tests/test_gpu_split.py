@@ -277,3 +277,35 @@ def test_short_or_missing_workspace_is_refused_before_launch():
         fa.fluxattn_forward_ex_bf16(q, k, v, o=o, split=fa.SplitWorkspace(g, 0))
     torch.cuda.synchronize()
     check_close(f64(o), attention_ref(inp), BF16_TOL, "uncut setting, no workspace")
+
+
+def test_split_default_setting_between_one_and_two_rounds():
+    """B=1, H=18, N = 512 + 64x64 = 4608: 324 query blocks, 1.27 rounds of
+    256 compute units, the second round 27% full.  The default setting runs
+    one whole round and cuts the other 68 blocks into pieces shared by all
+    workgroups (shares of about 19 key tiles, so each block has several
+    pieces).  It differs bitwise from the uncut launch (the cut happened),
+    stays close to it, leaves the counts at zero and matches the oracle on
+    rows of every query block of a whole-round head (0) and of the heads
+    the tail covers (14, 17).  At H=24 (432 blocks, the second round 69%
+    full) the default runs uncut."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"shape chosen for 256 compute units, device has {cus}")
+    assert fa.split_workspace(1, 24, 4608, 0).nbytes == 0
+    w = custom_workload(1, 18, 512, (64, 64))
+    inp = make_inputs(w)
+    ws = fa.split_workspace(1, 18, w.N, 0)
+    assert ws.nbytes > 0
+    o = forward_bf16(inp, ws)
+    whole = forward_bf16(inp)
+    torch.cuda.synchronize()
+    assert not torch.equal(o.view(torch.int16), whole.view(torch.int16))
+    close_to_uncut(o, whole, "bf16", "default setting H=18 N=4608")
+    assert not ws.counts().any()
+    rows = np.unique(np.concatenate([np.arange(0, w.N, 256)[:, None] + np.array([0, 131, 255])]).ravel())
+    rows = rows[rows < w.N]
+    for h in (0, 14, 17):
+        sl = (slice(0, 1), slice(h, h + 1))
+        ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
+        check_close(f64(o[sl])[:, :, rows], ref, BF16_TOL, f"default setting H=18 N=4608 head {h}")
