@@ -18,8 +18,7 @@ Prints one JSON line: TFLOP/s of the step (4*B*H*N^2*d per step), the
 attention kernel's roofline fraction (its own mean launch time from HIP
 events on the launch stream; median and minimum beside it), the sustained
 graphics clock and power over a second of back-to-back launches (amdsmi),
-the prologue's GB/s warm (its launches back to back between two events)
-and with the MALL flushed before every launch,
+the prologue's GB/s warm and with the MALL flushed before every launch,
 the matrix cores' MFMA-only rate on the same shapes under "mfma_ceiling"
 (fluxattn_probe_mfma, with clock and power) and each kernel's fraction of it,
 the same figures at N=4608 (FLUX-dev 1024x1024)
@@ -317,16 +316,6 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
     assert torch.isfinite(o).all().item()
     if ws is not None and ws.nbytes:
         assert not ws.counts().any().item(), "split arrival counts left non-zero"
-    # the prologue alone, `steps` launches back to back between two events:
-    # its launches take tens of microseconds, and events around each one add
-    # a few microseconds of their own (the per-step figure is kept beside)
-    e_b2b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e_b2b[0].record(stream)
-    for _ in range(steps):
-        prologue()
-    e_b2b[1].record(stream)
-    torch.cuda.synchronize()
-    t_pro_b2b = e_b2b[0].elapsed_time(e_b2b[1]) * 1e-3 / steps
     # the prologue with the 256 MB MALL flushed before every launch: a
     # 512 MiB fill between launches, outside the events
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -357,9 +346,9 @@ def run_gpu(name: str, steps: int, warmup: int, path: str = "fused", groups: int
         "forward_ms_median": t_fwd_med * 1e3,
         "forward_ms_min": t_fwd_min * 1e3,
         "forward_tflops": flops / t_fwd / 1e12,
-        "prologue_us": t_pro_b2b * 1e6,
-        "prologue_us_in_step_median": t_pro_med * 1e6,
-        "prologue_gbs": prologue_bytes / t_pro_b2b / 1e9,
+        "prologue_us": t_pro * 1e6,
+        "prologue_us_median": t_pro_med * 1e6,
+        "prologue_gbs": prologue_bytes / t_pro_med / 1e9,
         "prologue_gbs_mall_flushed": prologue_bytes / t_cold_med / 1e9,
         "prologue_bytes": prologue_bytes,
         "flops": flops,
@@ -543,8 +532,7 @@ def main():
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
                 "frac": round(r["prologue_gbs"] / HBM_PEAK_GBS, 4),
-                "launch_us": round(r["prologue_us"], 2),
-                "launch_us_in_step_median": round(r["prologue_us_in_step_median"], 2),
+                "launch_us_median": round(r["prologue_us_median"], 2),
             },
             "split_workspace_bytes": r["split_workspace_bytes"],
             "warmup_steps": r["warmup_steps"],
@@ -643,8 +631,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(main_res["prologue_gbs"] / HBM_PEAK_GBS, 4),
-            "launch_us": round(main_res["prologue_us"], 2),
-            "launch_us_in_step_median": round(main_res["prologue_us_in_step_median"], 2),
+            "launch_us_median": round(main_res["prologue_us_median"], 2),
         },
         "also": also,
         "fp8": fp8,
