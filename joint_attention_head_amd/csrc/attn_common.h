@@ -89,9 +89,9 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int total) {
 }
 
 // ---- Key-range split.  Without a split, the launch has whole_groups
-// persistent workgroups, the same number on every XCD but for the last
-// partial row of eight; the workgroups of XCD x take its contiguous range of
-// blocks (as xcd_logical_block deals them), in turn.  With split_groups = G
+// persistent workgroups, which the dispatcher deals to the 8 XCDs round
+// robin; those on XCD x take the blocks of its contiguous range (the range
+// xcd_logical_block gives it) in turn.  With split_groups = G
 // persistent workgroups and nb blocks, the first F = split_whole rounds
 // (chosen on the host, F G < nb) go as whole blocks in launch order:
 // workgroup w takes blocks w, w + G, ..., so the workgroups running at one
