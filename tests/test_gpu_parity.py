@@ -391,6 +391,47 @@ def test_forward_bf16_writes_every_output_and_nothing_else():
     assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
 
 
+# Uncut launches run as a persistent grid of one workgroup per compute unit,
+# each taking whole blocks of its XCD's range in turn.  Block counts above
+# the compute units and not a multiple of 8 (uneven XCD ranges): 259 = 37
+# heads x 7 blocks (N = 1792) and 513 = 3 x 19 x 9 (N = 2304).
+PERSIST_SHAPES = {"nb259": (1, 37, 512, (32, 40)), "nb513": (3, 19, 512, (32, 56))}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("shape", list(PERSIST_SHAPES))
+def test_forward_persistent_grid_covers_every_block(shape, dtype):
+    B, H, n_txt, grid = PERSIST_SHAPES[shape]
+    _flush(f"persistent grid {shape} {dtype}")
+    inp = small(B, H, n_txt, grid, None, dtype, seed=3)
+    N, D = inp.q.shape[2], inp.q.shape[3]
+    n = B * H * N * D
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    o = buf[guard:guard + n].view(B, H, N, D)
+    if dtype == "bf16":
+        fa.fluxattn_forward_bf16(dev(inp.q), dev(inp.k), dev(inp.v), o=o)
+    else:
+        fa.fluxattn_forward_fp8(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.q_scale), dev(inp.k_scale),
+                                dev(inp.v_scale), o=o)
+    torch.cuda.synchronize()
+    # every block written, nothing outside
+    assert torch.isfinite(o).all()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+    # rows of every query block of the first, a middle and the last head
+    rows = np.unique(np.concatenate([np.arange(0, N, 256)[:, None] + np.array([0, 77, 255])]).ravel())
+    rows = rows[rows < N]
+    tol = BF16_TOL if dtype == "bf16" else FP8_TOL
+    for b, h in ((0, 0), (B // 2, H // 2), (B - 1, H - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        if dtype == "bf16":
+            ref = oracle.attention(f64(inp.q[sl]), f64(inp.k[sl]), f64(inp.v[sl]), rows=rows)
+        else:
+            ref = oracle.attention(f64(inp.q[sl], inp.q_scale[sl]), f64(inp.k[sl], inp.k_scale[sl]),
+                                   f64(inp.v[sl], inp.v_scale[sl]), rows=rows)
+        check_close(f64(o[sl])[:, :, rows], ref, tol, f"persistent grid {shape} {dtype} head ({b},{h})")
+
+
 def test_forward_bf16_key_permutation_invariance():
     inp = small(1, 2, 11, (12, 12))
     perm = torch.randperm(inp.q.shape[2], generator=torch.Generator().manual_seed(1))
