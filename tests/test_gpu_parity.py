@@ -619,6 +619,39 @@ def test_joint_fused_bf16_t2i_2048_sampled():
     check_close(got2, joint_ref(inp, heads, rows), BF16_TOL, "joint fused bf16 t2i sampled (uncut)")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_joint_fused_flux_dev_1024_sampled(dtype):
+    """The launches the benchmark times at FLUX-dev 1024x1024 (B=1, H=24,
+    N = 512 + 64x64 = 4608), in both precisions: keys-only prologue, then
+    the fused attention with the default split setting, which leaves this
+    launch uncut: 432 query blocks on a persistent grid of one workgroup per
+    compute unit, 176 workgroups taking a second block with a job start that
+    overlaps the query transform with the first tile copies.  Rows of every
+    query block of three heads against the whole fp64 chain."""
+    _flush(f"joint fused {dtype} flux_dev_1024 (N=4608), benchmark launches")
+    w = custom_workload(1, 24, 512, (64, 64), None, dtype)
+    inp = make_inputs(w)
+    B, H, N = inp.q.shape[:3]
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    w_q, w_k, pos = dev(inp.w_q), dev(inp.w_k), dev(inp.pos)
+    ws = fa.split_workspace(B, H, N, 0)
+    if dtype == "bf16":
+        _, kn = fa.fluxattn_qk_norm_rope_bf16(None, k, None, w_k, pos)
+        o = fa.fluxattn_forward_fused_ex_bf16(q, kn, v, w_q, pos, split=ws)
+        tol, bound = BF16_TOL, 1e-2
+    else:
+        sq, sk, sv = dev(inp.q_scale), dev(inp.k_scale), dev(inp.v_scale)
+        _, kn, _, skn = fa.fluxattn_qk_norm_rope_fp8(None, k, None, sk, None, w_k, pos)
+        o = fa.fluxattn_forward_fused_ex_fp8(q, kn, v, sq, skn, sv, w_q, pos, split=ws)
+        tol, bound = FP8_TOL, 1e-1
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 12), (0, 23)]
+    rows = block_rows(N, offsets=(0, 255))
+    got = np.stack([f64(o[b, h, torch.from_numpy(rows)]) for (b, h) in heads])
+    rel = check_close(got, joint_ref(inp, heads, rows), tol, f"joint fused {dtype} flux_dev_1024 sampled")
+    assert rel < bound
+
+
 def test_joint_fused_fp8_parity():
     """fp8 with the fused query prologue (Q' re-encoded in E4M3 per query
     inside the attention kernel) against the fp64 chain, and close to the
