@@ -9,7 +9,7 @@ tokens = 16896, d=128, bf16), inputs already resident in HBM.  Default path
 that normalises and rotates the queries as it loads them; --path unfused
 runs the prologue on both and the plain attention kernel.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10]
 
 The attention launches use the key-range split with a workspace allocated
 (zeroed) before the timed region (--groups, default 0: the library's rule).
@@ -128,7 +128,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="t2i_2048_cfg")
     p.add_argument("--also", default="flux_dev_1024", help="second metric point ('' to skip)")
     p.add_argument("--fp8", default="i2i_2048", help="fp8 workload ('' to skip)")
